@@ -1,0 +1,59 @@
+"""Pins of the oracle's log-normaliser and of the probabilities it reports.
+
+The tempered softmax is fixed by the sampling rule (softmax(z / T) on both
+sides).  The oracle's value is checked against scipy's logsumexp, an
+independent library routine, and against exact invariances.
+"""
+import numpy as np
+import pytest
+from scipy import special
+
+import workloads as W
+
+
+def _rows(rng, n, V, dtype, scale):
+    z = (rng.standard_normal((n, V)) * scale).astype(np.float32)
+    return W.bf16_bits(z) if dtype == "bf16" else z
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.7, 0.8, 1.0, 2.0])
+def test_log_normaliser_matches_scipy(orc, dtype, T):
+    rng = np.random.default_rng(11)
+    for row in _rows(rng, 6, 5000, dtype, 3.0):
+        z = W.as_f32(row).astype(np.float64)
+        ref = special.logsumexp(z / T)
+        got = orc.row_log_normaliser(row, T)
+        assert abs(got - ref) <= 1e-13 * max(1.0, abs(ref)), (got, ref)
+
+
+def test_log_normaliser_masked_entries(orc):
+    z = np.full(100, -np.inf, np.float32)
+    z[[3, 50]] = [1.0, 2.0]
+    ref = special.logsumexp(np.array([1.0, 2.0]) / 0.5)
+    assert abs(orc.row_log_normaliser(z, 0.5) - ref) < 1e-14
+
+
+def test_temperature_power_of_two_is_exact(orc):
+    """softmax_T(z) = softmax_1(z / T): for T = 1/2 the scaled row 2z is exact in
+    bf16, so both evaluations run the same arithmetic and agree to the bit."""
+    rng = np.random.default_rng(3)
+    for row in _rows(rng, 4, 3000, "bf16", 2.0):
+        z = W.as_f32(row)
+        doubled = W.bf16_bits(2.0 * z)
+        np.testing.assert_array_equal(W.as_f32(doubled), 2.0 * z)
+        assert orc.row_log_normaliser(row, 0.5) == orc.row_log_normaliser(doubled, 1.0)
+
+
+def test_reported_probabilities_match_scipy(orc):
+    case = W.make_case("p", b=3, K=4, V=3000, dtype="bf16", target_scale=2.5,
+                       draft_sigma=0.7, T=0.7, seed=5)
+    res = orc.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
+    for s in range(case.b):
+        for i in range(case.K):
+            x = case.draft_tokens[s, i]
+            p = special.softmax(W.as_f32(case.target[s, i]).astype(np.float64) / case.T)[x]
+            q = special.softmax(W.as_f32(case.draft[s, i]).astype(np.float64) / case.T)[x]
+            assert res["p_draft"][s, i] == pytest.approx(p, rel=1e-12)
+            assert res["q_draft"][s, i] == pytest.approx(q, rel=1e-12)
+            assert res["r"][s, i] == pytest.approx(p / q, rel=1e-11)

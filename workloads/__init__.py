@@ -1,0 +1,248 @@
+"""Seeded synthetic inputs for the verify/accept step.
+
+This module only produces input bytes: target logit blocks [b, K+1, V], draft
+logit blocks [b, K, V], draft tokens [b, K], per-sequence Philox seeds and the
+per-sequence rule (greedy or sampling).  It holds none of the accept rule's
+arithmetic and serves the tests, the benchmark and the oracle alike.
+
+Draft tokens are produced the way a drafter would produce them: the argmax of
+the stored draft row (greedy rows) or a draw from softmax(z_d / T) of the
+stored draft row (sampling rows), the draw taken with the Gumbel-max trick
+(argmax of z_d / T + Gumbel noise, Gumbel's 1954 extreme-value construction),
+so no softmax is evaluated here.  All randomness is numpy PCG64.
+
+Stored logits are bf16 (returned as their raw uint16 bit patterns, rounded to
+nearest even from float32) or float32.
+
+The five named workloads mirror the shapes of the pages' own settings: a
+262144-entry vocabulary and a 7-token block (the Gemma-4 DSpark drafter
+arguments, "dspark-mlx 0.1.0" wheel diff, dspark_mlx/arch/gemma4.py), and a
+draft cap of 4 ("mlx-dspark 0.0.1" README, Tuning).  They stand in for the
+pages' end-to-end decoding workloads (prompt suites that are not available
+here): logits are synthetic, drawn as described per workload.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+GREEDY = 0
+SAMPLING = 1
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    # process in slabs to bound temporaries
+    flat_u = u.reshape(-1)
+    flat_o = out.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat_u.size, step):
+        s = flat_u[i:i + step]
+        nan = (s & 0x7FFFFFFF) > 0x7F800000
+        r = (s + (0x7FFF + ((s >> 16) & 1))) >> 16
+        r = r.astype(np.uint16)
+        r[nan] = ((s[nan] >> 16) | 0x0040).astype(np.uint16)  # keep NaN quiet
+        flat_o[i:i + step] = r
+    return out
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f32(a: np.ndarray) -> np.ndarray:
+    """Stored logits (float32 or bf16 bits) as float32 values."""
+    return a if a.dtype == np.float32 else bf16_to_f32(a)
+
+
+@dataclass
+class Case:
+    """One verify batch: every array is host memory (numpy)."""
+    name: str
+    dtype: str                      # "f32" or "bf16"
+    b: int
+    K: int
+    V: int
+    T: float
+    target: np.ndarray              # [b, K+1, V] float32 or uint16 bf16 bits
+    draft: np.ndarray               # [b, K, V]
+    draft_tokens: np.ndarray        # [b, K] int32
+    seeds: np.ndarray               # [b] uint64
+    rule: np.ndarray                # [b] GREEDY / SAMPLING
+    meta: dict = field(default_factory=dict)
+
+    def rows(self, rule: int) -> np.ndarray:
+        return np.nonzero(self.rule == rule)[0]
+
+    def take(self, idx: Sequence[int]) -> "Case":
+        idx = np.asarray(idx)
+        return Case(self.name, self.dtype, len(idx), self.K, self.V, self.T,
+                    np.ascontiguousarray(self.target[idx]),
+                    np.ascontiguousarray(self.draft[idx]),
+                    np.ascontiguousarray(self.draft_tokens[idx]),
+                    np.ascontiguousarray(self.seeds[idx]),
+                    np.ascontiguousarray(self.rule[idx]), dict(self.meta))
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+def _zipf_rows(rng: np.random.Generator, nrows: int, V: int, slope: float,
+               jitter: float) -> np.ndarray:
+    """Rows whose sorted log-probabilities fall as -slope*ln(rank), ranks in a
+    random order per row, plus N(0, jitter^2)."""
+    base = (-slope * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
+    out = np.empty((nrows, V), np.float32)
+    for r in range(nrows):
+        out[r] = base[rng.permutation(V)]
+        out[r] += rng.standard_normal(V, dtype=np.float32) * np.float32(jitter)
+    return out
+
+
+def _gumbel_draw(rng: np.random.Generator, z: np.ndarray, T: float) -> int:
+    """One draw from softmax(z / T) by the Gumbel-max trick."""
+    u = rng.random(z.shape[-1], dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        g = -np.log(-np.log(u))
+    return int(np.argmax(z.astype(np.float64) / T + g))
+
+
+def make_case(name: str, *, b: int, K: int, V: int, dtype: str = "bf16",
+              target_kind: str = "normal", target_scale: float = 1.0,
+              zipf_slope: float = 1.1, zipf_jitter: float = 0.3,
+              draft_sigma: Union[float, Tuple[float, float]] = 0.5,
+              rule: Union[int, Sequence[int]] = SAMPLING, T: float = 1.0,
+              seed: int = 0, philox_seeds: Optional[Sequence[int]] = None,
+              equal_draft_rows: Sequence[int] = (), spike_prob: float = 0.0,
+              spike_height: float = 20.0, greedy_draft: str = "argmax") -> Case:
+    """Generate one seeded batch.
+
+    target_kind  "normal": iid N(0, target_scale^2); "zipf": see _zipf_rows.
+    draft_sigma  scalar, or (lo, hi) for a per-sequence sigma ~ U[lo, hi];
+                 draft = target (before rounding) + N(0, sigma^2).
+    rule         per-sequence GREEDY / SAMPLING (scalar = all the same).
+    equal_draft_rows  sequences whose draft block is bitwise the target's first K rows.
+    spike_prob   each target row gets +spike_height on one uniform token with
+                 this probability (at least one row when > 0); drafts are
+                 derived from the rows before the spike.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if np.isscalar(rule):
+        rules = np.full(b, int(rule), np.int32)
+    else:
+        rules = np.asarray(rule, np.int32)
+        assert rules.shape == (b,)
+    if isinstance(draft_sigma, tuple):
+        sig = rng.uniform(draft_sigma[0], draft_sigma[1], size=b)
+    else:
+        sig = np.full(b, float(draft_sigma))
+
+    tgt_bits = None
+    tgt_f = np.empty((b, K + 1, V), np.float32)
+    drf_f = np.empty((b, K, V), np.float32)
+    for s in range(b):
+        if target_kind == "normal":
+            rows = rng.standard_normal((K + 1, V), dtype=np.float32) * np.float32(target_scale)
+        elif target_kind == "zipf":
+            rows = _zipf_rows(rng, K + 1, V, zipf_slope, zipf_jitter)
+        else:
+            raise ValueError(target_kind)
+        tgt_f[s] = rows
+        noise = rng.standard_normal((K, V), dtype=np.float32) * np.float32(sig[s])
+        drf_f[s] = rows[:K] + noise
+
+    spiked = []
+    if spike_prob > 0.0:
+        hits = rng.random(b * (K + 1)) < spike_prob
+        if not hits.any():
+            hits[rng.integers(b * (K + 1))] = True
+        for flat in np.nonzero(hits)[0]:
+            s, i = divmod(int(flat), K + 1)
+            v = int(rng.integers(V))
+            tgt_f[s, i, v] += np.float32(spike_height)
+            spiked.append((s, i, v))
+
+    if dtype == "bf16":
+        target = bf16_bits(tgt_f)
+        draft = bf16_bits(drf_f)
+    elif dtype == "f32":
+        target = tgt_f
+        draft = drf_f
+    else:
+        raise ValueError(dtype)
+    del tgt_f, drf_f
+    for s in equal_draft_rows:
+        draft[s] = target[s, :K]
+
+    tokens = np.empty((b, K), np.int32)
+    for s in range(b):
+        for i in range(K):
+            z = as_f32(draft[s, i])
+            if rules[s] == GREEDY and greedy_draft == "argmax":
+                tokens[s, i] = int(np.argmax(z))
+            else:
+                tokens[s, i] = _gumbel_draw(rng, z, T)
+
+    if philox_seeds is None:
+        seeds = np.arange(b, dtype=np.uint64)
+    else:
+        seeds = np.asarray(philox_seeds, dtype=np.uint64)
+    meta = {"draft_sigma": sig, "spiked": spiked, "seed": seed,
+            "target_kind": target_kind}
+    return Case(name, dtype, b, K, V, float(T), target, draft, tokens, seeds, rules, meta)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.  Data seed 1000 * id + 1.
+
+CONFIG_TEXT = {
+    1: "b=1 K=7 V=151936 fp32, target N(0,2^2), draft = target + N(0,0.5^2), "
+       "tokens ~ draft softmax, T=1.0, Philox seed 0, greedy and sampling",
+    2: "b=8 K=7 V=262144 bf16, Zipf target (-1.1 ln rank + N(0,0.3^2)), "
+       "draft = target + N(0,0.8^2), tokens = draft argmax, greedy",
+    3: "b=32 K=7 V=151936 bf16, target N(0,2.5^2), per-row draft sigma ~ U[0.2,1.5], "
+       "sampling T=0.7, Philox seed per row",
+    4: "b=64 K=4 V=129280 bf16, Zipf target, draft = target + N(0,0.5^2), rows 0..31 "
+       "draft == target, sampling T=1.0",
+    5: "b=128 K=7 V=262144 bf16, target N(0,3^2) with 1% of rows spiked +20, per-row "
+       "draft sigma ~ U[0.1,2.0], rows 0..63 greedy / 64..127 sampling, T=0.8",
+}
+
+
+def config(cid: int, b: Optional[int] = None, V: Optional[int] = None) -> Case:
+    """Workload `cid` (1..5).  `b` / `V` shrink it for quick runs (same recipe)."""
+    seed = 1000 * cid + 1
+    if cid == 1:
+        bb, VV = b or 1, V or 151936
+        # b=1: both rules run on the same sequence; rule marks the sampling call.
+        return make_case("c1", b=bb, K=7, V=VV, dtype="f32", target_kind="normal",
+                         target_scale=2.0, draft_sigma=0.5, rule=SAMPLING, T=1.0,
+                         seed=seed, philox_seeds=[0] * bb)
+    if cid == 2:
+        bb, VV = b or 8, V or 262144
+        return make_case("c2", b=bb, K=7, V=VV, dtype="bf16", target_kind="zipf",
+                         draft_sigma=0.8, rule=GREEDY, T=1.0, seed=seed)
+    if cid == 3:
+        bb, VV = b or 32, V or 151936
+        return make_case("c3", b=bb, K=7, V=VV, dtype="bf16", target_kind="normal",
+                         target_scale=2.5, draft_sigma=(0.2, 1.5), rule=SAMPLING,
+                         T=0.7, seed=seed)
+    if cid == 4:
+        bb, VV = b or 64, V or 129280
+        return make_case("c4", b=bb, K=4, V=VV, dtype="bf16", target_kind="zipf",
+                         draft_sigma=0.5, rule=SAMPLING, T=1.0, seed=seed,
+                         equal_draft_rows=range(bb // 2))
+    if cid == 5:
+        bb, VV = b or 128, V or 262144
+        rules = np.array([GREEDY] * (bb // 2) + [SAMPLING] * (bb - bb // 2), np.int32)
+        return make_case("c5", b=bb, K=7, V=VV, dtype="bf16", target_kind="normal",
+                         target_scale=3.0, draft_sigma=(0.1, 2.0), rule=rules, T=0.8,
+                         seed=seed, spike_prob=0.01)
+    raise ValueError(f"unknown workload {cid}")

@@ -1,0 +1,150 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) verify/accept library for block
+ * speculative decoding.
+ *
+ * One decode cycle hands the accept policy a target logit block [K+1, V] per
+ * sequence: row 0 is p_1 from the anchor step, rows 1..K are p_2..p_{K+1}
+ * from one verify forward over the K drafted tokens, row K being the bonus
+ * position ("dspark-mlx 0.1.0" wheel diff, dspark_mlx/adapter.py, module
+ * docstring "Logit conventions").  The policy exports greedy_accept and
+ * speculative_sample_accept returning an AcceptResult (same page,
+ * dspark_mlx/__init__.py); the accepted count is what
+ * BaseModelAdapter.kv_rollback(n_keep) consumes (same page, adapter.py).
+ *
+ * Conventions shared by every entry point:
+ *  - Logit pointers, token, seed and output pointers are DEVICE pointers; the
+ *    caller owns every buffer, the workspace included.  The library never
+ *    allocates, never synchronises, and enqueues its kernels only on
+ *    `hip_stream` (a hipStream_t; NULL is the default stream).  Outputs are
+ *    valid once the stream reaches that point.
+ *  - Logits are fp32 or bf16 (dtype), laid out [b, rows, V] with V
+ *    contiguous; strides are in ELEMENTS.  `*_row_stride` >= V,
+ *    `*_batch_stride` >= 0.  Base pointers must be aligned to the element
+ *    size.  Rows that start on 16-byte boundaries take 16-byte vector loads;
+ *    other layouts take an element-wise path with identical results.
+ *  - Argument errors are reported before anything is enqueued.  Per-sequence
+ *    data errors never fail the call: a sequence whose rows hold NaN or +inf,
+ *    or a row with no finite entry, or a draft token outside [0, V), gets
+ *    n_accepted = -1, all its tokens -1 and NaN probabilities.  -inf logits
+ *    (masked vocabulary) are allowed.
+ *  - Calls are thread-safe and keep no state between calls.  Calls that share
+ *    one workspace must be ordered on one stream.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = 1,   /* bad size, stride, temperature, null pointer, small workspace */
+    SPEC_EDTYPE = 2,   /* unknown dtype code */
+    SPEC_EALIGN = 3,   /* a logit base pointer not aligned to its element size */
+    SPEC_ELAUNCH = 4   /* the HIP runtime refused a kernel launch */
+} spec_status;
+
+typedef enum {
+    SPEC_F32 = 0,
+    SPEC_BF16 = 1
+} spec_dtype;
+
+/* Largest block length K accepted by the entry points. */
+#define SPEC_MAX_K 32
+
+/*
+ * Bytes of device workspace one call needs for batch b, block length K and
+ * vocabulary V (sampling != 0 for spec_sample_accept).  Returns 0 when the
+ * sizes are out of range (b < 1, K < 1, K > SPEC_MAX_K, V < 1) or the dtype
+ * is unknown.  The workspace needs no initialisation; 256-byte alignment.
+ */
+size_t spec_workspace_bytes(int b, int K, int V, int dtype, int sampling);
+
+/* Static description of a status code (never NULL). */
+const char *spec_status_string(int status);
+
+/*
+ * Greedy accept ("greedy-correct by construction": the committed tokens are
+ * the target's own argmax chain, identical to plain greedy decoding up to
+ * exact ties -- "mlx-dspark 0.0.1" sdist diff, README "How it works";
+ * benchmark.py's plain greedy token is argmax of the raw logits).
+ *
+ * For each sequence s: A_i = lowest index of the largest raw logit of target
+ * row i (i = 0..K); n = length of the longest prefix with x_i == A_i;
+ * tokens[s] = (x_0 .. x_{n-1}, A_n, -1, ..., -1) (K+1 entries).
+ *
+ *   target          [b, K+1, V] logits (device), element strides below
+ *   draft_tokens    [b, K] int32 (device)
+ *   n_accepted      [b] int32 out (device)
+ *   tokens          [b, K+1] int32 out (device)
+ *   target_argmax   [b, K+1] int32 out (device) or NULL: A_i of every row
+ *   workspace       spec_workspace_bytes(b, K, V, dtype, 0) bytes (device)
+ */
+int spec_greedy_accept(const void *target, int dtype,
+                       int64_t t_batch_stride, int64_t t_row_stride,
+                       const int32_t *draft_tokens, int b, int K, int V,
+                       int32_t *n_accepted, int32_t *tokens, int32_t *target_argmax,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Lossless speculative-sampling accept (the published rule of Leviathan,
+ * Kalman & Matias 2023 and Chen et al. 2023; the pages call the policy
+ * lossless: "dspark-mlx 0.1.0", adapter.py docstring, and the
+ * "DeepSeek-V4-Flash DSpark drafter" model card).
+ *
+ * With p_i = softmax(target row i / T) and q_i = softmax(draft row i / T):
+ * slot i < K accepts x_i iff u_i < min(1, p_i(x_i) / q_i(x_i)), where
+ * u_i = U(seed_s, s, i, 0); n = index of the first rejected slot, else K.
+ * When n < K the token at slot n is drawn from normalise(max(0, p_n - q_n));
+ * when n == K it is drawn from p_{K+1} (the bonus); in both cases by inverse
+ * CDF in ascending vocabulary order with t = U(seed_s, s, n, 1) * R, R the
+ * total mass.  U(seed, row, pos, tag) = (w >> 8) * 2^-24 with w the first
+ * output word of Philox4x32-10 (Salmon et al., SC'11) at counter
+ * (pos, row, tag, 0) and key (low, high 32 bits of seed); `row` is the
+ * sequence index inside this call.
+ *
+ *   target          [b, K+1, V] logits (device)
+ *   draft           [b, K, V] logits of the same dtype (device)
+ *   draft_tokens    [b, K] int32 (device), drawn by the caller from q
+ *   temperature     T > 0, finite; divides the logits of both sides
+ *   seeds           [b] uint64 (device), one Philox key per sequence
+ *   n_accepted      [b] int32 out; tokens [b, K+1] int32 out (-1 padded)
+ *   p_draft, q_draft  [b, K] float out or NULL: p_i(x_i), q_i(x_i) of every slot
+ *   workspace       spec_workspace_bytes(b, K, V, dtype, 1) bytes (device)
+ */
+int spec_sample_accept(const void *target, const void *draft, int dtype,
+                       int64_t t_batch_stride, int64_t t_row_stride,
+                       int64_t d_batch_stride, int64_t d_row_stride,
+                       const int32_t *draft_tokens, int b, int K, int V,
+                       double temperature, const uint64_t *seeds,
+                       int32_t *n_accepted, int32_t *tokens,
+                       float *p_draft, float *q_draft,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Profiling hook (not part of the accept semantics).  Registers, for the
+ * calling host thread only, an array of n_events hipEvent_t handles.  While
+ * registered, each accept call records events[0] before its first kernel and
+ * events[k] after its k-th kernel (k = 1 .. number of kernels, 2 for greedy,
+ * 4 for sampling) on its stream, if n_events is large enough; otherwise it
+ * records nothing.  Pass NULL / 0 to unregister.  Returns SPEC_OK.
+ */
+int spec_set_stage_events(void *const *events, int n_events);
+
+/*
+ * Plain device copy of nbytes (a multiple of 16, 16-byte aligned pointers)
+ * with the same 16-byte load path as the row pass, enqueued on hip_stream.
+ * Used to calibrate hardware byte counters and to measure the achievable
+ * streaming bandwidth.  Returns SPEC_EINVAL / SPEC_ELAUNCH on error.
+ */
+int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

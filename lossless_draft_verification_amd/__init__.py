@@ -1,0 +1,220 @@
+"""Verify/accept for block speculative decoding on MI355X (gfx950).
+
+Python binding of the C ABI in ``include/specverify.h``: argument marshalling
+only.  Every step of the accept path runs in the HIP kernels of
+``libspecverify.so``; PyTorch provides device memory and streams.
+
+The names mirror the accept policy's exports on "dspark-mlx 0.1.0" wheel
+diff, dspark_mlx/__init__.py: ``greedy_accept``,
+``speculative_sample_accept`` and ``AcceptResult``.  Their input is the
+target logit block [b, K+1, V] (row 0 = p_1 from the anchor step, rows
+1..K = p_2..p_{K+1} from one verify forward, row K the bonus position; same
+page, dspark_mlx/adapter.py, "Logit conventions"), the drafter's [b, K, V]
+logits and its K tokens.  ``n_accepted`` is the ``n_keep`` that
+``BaseModelAdapter.kv_rollback`` takes; the committed tokens are
+``tokens[:, :n_accepted + 1]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "workspace_bytes",
+           "set_stage_events", "stream_copy", "library_path", "SpecError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_MAX_K = 32
+
+
+class SpecError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz, dbl = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_double)
+    lib.spec_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.spec_workspace_bytes.restype = sz
+    lib.spec_status_string.argtypes = [i32]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_greedy_accept.argtypes = [vp, i32, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.spec_greedy_accept.restype = i32
+    lib.spec_sample_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, dbl, vp,
+                                       vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_sample_accept.restype = i32
+    lib.spec_set_stage_events.argtypes = [vp, i32]
+    lib.spec_set_stage_events.restype = i32
+    lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.spec_stream_copy.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise SpecError(f"status {rc}: {_lib.spec_status_string(rc).decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def _on_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("every tensor must live on the GPU")
+
+
+@dataclass
+class AcceptResult:
+    """Result of one accept call (device tensors).
+
+    n_accepted  [b] int32: accepted draft tokens (-1 for an invalid sequence)
+    tokens      [b, K+1] int32: committed tokens, -1 after position n_accepted
+    p_draft     [b, K] float32: p_i(x_i) of every slot (sampling rule)
+    q_draft     [b, K] float32: q_i(x_i) of every slot (sampling rule)
+    argmax      [b, K+1] int32: target argmax of every row (greedy rule)
+    """
+    n_accepted: torch.Tensor
+    tokens: torch.Tensor
+    p_draft: Optional[torch.Tensor] = None
+    q_draft: Optional[torch.Tensor] = None
+    argmax: Optional[torch.Tensor] = None
+
+
+def workspace_bytes(b: int, K: int, V: int, dtype: torch.dtype, sampling: bool) -> int:
+    code = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
+    n = _lib.spec_workspace_bytes(b, K, V, code, int(bool(sampling)))
+    if n == 0:
+        raise ValueError(f"sizes out of range: b={b} K={K} V={V}")
+    return n
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
+    return ws
+
+
+def greedy_accept(target: torch.Tensor, draft_tokens: torch.Tensor, *, want_argmax: bool = True,
+                  out: Optional[AcceptResult] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> AcceptResult:
+    """Greedy accept of target [b, K+1, V] against draft tokens [b, K]."""
+    _on_gpu(target, draft_tokens)
+    if target.dim() != 3 or target.stride(2) != 1:
+        raise ValueError("target must be [b, K+1, V] with V contiguous")
+    b, K1, V = target.shape
+    K = K1 - 1
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    dev = target.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           argmax=torch.empty(b, K1, dtype=torch.int32, device=dev) if want_argmax else None)
+    need = workspace_bytes(b, K, V, target.dtype, False)
+    ws = _workspace(workspace, need, dev)
+    rc = _lib.spec_greedy_accept(
+        target.data_ptr(), _dtype_code(target), target.stride(0), target.stride(1),
+        draft_tokens.data_ptr(), b, K, V, out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.argmax.data_ptr() if out.argmax is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+def speculative_sample_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                              temperature: float, seeds: torch.Tensor, *,
+                              out: Optional[AcceptResult] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> AcceptResult:
+    """Lossless speculative-sampling accept; temperature 0 falls back to greedy.
+
+    seeds: [b] int64 or uint64 Philox keys (bit patterns are used as given).
+    """
+    if temperature == 0.0:
+        return greedy_accept(target, draft_tokens, workspace=workspace, stream=stream)
+    _on_gpu(target, draft, draft_tokens, seeds)
+    if target.dim() != 3 or draft.dim() != 3 or target.stride(2) != 1 or draft.stride(2) != 1:
+        raise ValueError("target [b, K+1, V] and draft [b, K, V] need V contiguous")
+    b, K1, V = target.shape
+    K = K1 - 1
+    if draft.shape != (b, K, V) or draft.dtype != target.dtype:
+        raise ValueError("draft must be [b, K, V] with the target's dtype")
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    dev = target.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           p_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           q_draft=torch.empty(b, K, dtype=torch.float32, device=dev))
+    need = workspace_bytes(b, K, V, target.dtype, True)
+    ws = _workspace(workspace, need, dev)
+    rc = _lib.spec_sample_accept(
+        target.data_ptr(), draft.data_ptr(), _dtype_code(target), target.stride(0), target.stride(1),
+        draft.stride(0), draft.stride(1), draft_tokens.data_ptr(), b, K, V, float(temperature),
+        seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.p_draft.data_ptr() if out.p_draft is not None else None,
+        out.q_draft.data_ptr() if out.q_draft is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+_stage_keepalive = None
+
+
+def set_stage_events(events: Optional[Sequence[torch.cuda.Event]]) -> None:
+    """Register torch CUDA events as the calling thread's stage markers (see
+    spec_set_stage_events); None unregisters.  Events must already exist on
+    the device (record them once, or create them with enable_timing=True and
+    call .record() beforehand)."""
+    global _stage_keepalive
+    if not events:
+        _stage_keepalive = None
+        _check(_lib.spec_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+    _stage_keepalive = (arr, list(events))
+    _check(_lib.spec_set_stage_events(ctypes.cast(arr, ctypes.c_void_p), len(events)))
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Device copy through the library's 16-byte streaming kernel."""
+    _on_gpu(dst, src)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _check(_lib.spec_stream_copy(dst.data_ptr(), src.data_ptr(), n, _stream_handle(src.device, stream)))

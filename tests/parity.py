@@ -1,0 +1,170 @@
+"""Helpers shared by the GPU parity tests: move a seeded workload to the GPU,
+run the HIP path through the C ABI (via the Python binding), run the oracle
+on the same bytes, and compare element by element.
+
+Decisions are compared bit-exactly.  A disagreement is tolerated only when
+the oracle itself sits within a near-tie band of that decision, and every
+such case is counted and reported:
+
+* accept test of slot i: |u_i - min(1, r_i)| < 1e-6 (r_i the oracle's ratio);
+* drawn token (residual or bonus): the oracle's t lies within 1e-6 * R of a
+  step of the oracle's CDF between the two answers (R the total mass).
+
+After a tolerated disagreement the rest of that sequence is not compared.
+Probabilities p_i(x_i), q_i(x_i) must agree within 1e-5 relative.
+"""
+from __future__ import annotations
+
+import json
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+ACCEPT_BAND = 1e-6
+DRAW_BAND = 1e-6
+PROB_RTOL = 1e-5
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def seeds_to_device(seeds: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(seeds, dtype=np.uint64).view(np.int64)).to(device)
+
+
+@dataclass
+class Report:
+    sequences: int = 0
+    greedy_sequences: int = 0
+    sampling_sequences: int = 0
+    exact_sequences: int = 0
+    accept_slots_in_band: int = 0        # slots whose |u - min(1,r)| < band (reported, any outcome)
+    accept_near_tie_mismatch: int = 0    # tolerated accept-decision disagreements
+    draw_near_tie_mismatch: int = 0      # tolerated drawn-token disagreements
+    draws: int = 0
+    residual_draws: int = 0
+    bonus_draws: int = 0
+    max_prob_rel_err: float = 0.0
+    failures: list = field(default_factory=list)
+
+    def merge(self, o: "Report") -> "Report":
+        for k, v in o.__dict__.items():
+            if k == "failures":
+                self.failures += v
+            elif k == "max_prob_rel_err":
+                self.max_prob_rel_err = max(self.max_prob_rel_err, v)
+            else:
+                setattr(self, k, getattr(self, k) + v)
+        return self
+
+    def save(self, name: str) -> None:
+        out = os.environ.get("SPEC_PARITY_REPORT_DIR")
+        if out:
+            os.makedirs(out, exist_ok=True)
+            with open(os.path.join(out, f"{name}.json"), "w") as f:
+                json.dump(self.__dict__, f, indent=1, default=str)
+        print(f"[parity {name}] {json.dumps({k: v for k, v in self.__dict__.items() if k != 'failures'})}",
+              flush=True)
+
+
+def compare_greedy(case: W.Case, n_g, tok_g, am_g, name: str) -> Report:
+    n_o, tok_o, am_o = oracle.greedy_accept(case.target, case.draft_tokens)
+    rep = Report(sequences=case.b, greedy_sequences=case.b)
+    bad = np.nonzero((n_g != n_o) | (tok_g != tok_o).any(axis=1) | (am_g != am_o).any(axis=1))[0]
+    rep.exact_sequences = case.b - len(bad)
+    for s in bad[:10]:
+        rep.failures.append(dict(case=name, seq=int(s), n_gpu=int(n_g[s]), n_oracle=int(n_o[s]),
+                                 tok_gpu=tok_g[s].tolist(), tok_oracle=tok_o[s].tolist(),
+                                 am_gpu=am_g[s].tolist(), am_oracle=am_o[s].tolist()))
+    return rep
+
+
+def _draw_near_tie(case: W.Case, res: dict, s: int, slot: int, y_g: int) -> bool:
+    if y_g < 0 or y_g >= case.V:
+        return False
+    F = oracle.draw_cdf(case.target, case.draft, case.T, s, slot, bool(res["residual"][s]))
+    t, R, y_o = res["t"][s], res["R"][s], res["tokens"][s, slot]
+    if y_g > y_o:
+        margin = F[y_g - 1] - t
+    else:
+        margin = t - F[y_g]
+    return 0.0 <= margin <= DRAW_BAND * R
+
+
+def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str) -> Report:
+    res = oracle.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
+    n_o, tok_o = res["n_accepted"], res["tokens"]
+    rep = Report(sequences=case.b, sampling_sequences=case.b)
+    K = case.K
+    band = np.abs(res["u"] - np.minimum(1.0, res["r"])) < ACCEPT_BAND
+    for s in range(case.b):
+        # probabilities of every slot
+        if n_o[s] >= 0:
+            for arr_g, arr_o in ((p_g, res["p_draft"]), (q_g, res["q_draft"])):
+                g, o = arr_g[s].astype(np.float64), arr_o[s]
+                ok = np.isclose(g, o, rtol=PROB_RTOL, atol=1e-37)
+                rel = np.abs(g - o) / np.maximum(np.abs(o), 1e-300)
+                rep.max_prob_rel_err = max(rep.max_prob_rel_err, float(rel[o > 1e-30].max(initial=0.0)))
+                if not ok.all():
+                    rep.failures.append(dict(case=name, seq=s, what="probability", gpu=g.tolist(),
+                                             oracle=o.tolist()))
+        else:
+            if not (np.isnan(p_g[s]).all() and np.isnan(q_g[s]).all()):
+                rep.failures.append(dict(case=name, seq=s, what="invalid sequence probabilities"))
+        nb = int(band[s, :max(0, min(n_o[s], K - 1)) + 1].sum()) if n_o[s] >= 0 else 0
+        rep.accept_slots_in_band += nb
+        if n_o[s] >= 0:
+            rep.draws += 1
+            if n_o[s] < K:
+                rep.residual_draws += 1
+            else:
+                rep.bonus_draws += 1
+        if n_g[s] == n_o[s] and (tok_g[s] == tok_o[s]).all():
+            rep.exact_sequences += 1
+            continue
+        if n_g[s] != n_o[s]:
+            j = int(min(n_g[s], n_o[s]))
+            if n_o[s] >= 0 and n_g[s] >= 0 and j < K and band[s, j] and \
+                    (tok_g[s, :j] == tok_o[s, :j]).all():
+                rep.accept_near_tie_mismatch += 1
+                continue
+            rep.failures.append(dict(case=name, seq=s, what="accepted length", n_gpu=int(n_g[s]),
+                                     n_oracle=int(n_o[s]), u=res["u"][s].tolist(), r=res["r"][s].tolist()))
+            continue
+        n = int(n_o[s])
+        if (tok_g[s, :n] == tok_o[s, :n]).all() and (tok_g[s, n + 1:] == -1).all() and \
+                _draw_near_tie(case, res, s, n, int(tok_g[s, n])):
+            rep.draw_near_tie_mismatch += 1
+            continue
+        rep.failures.append(dict(case=name, seq=s, what="tokens", n=n, tok_gpu=tok_g[s].tolist(),
+                                 tok_oracle=tok_o[s].tolist(), t=float(res["t"][s]), R=float(res["R"][s])))
+    return rep
+
+
+def run_gpu_greedy(case: W.Case, target_dev=None):
+    import lossless_draft_verification_amd as L
+    t = to_device(case.target) if target_dev is None else target_dev
+    x = torch.from_numpy(case.draft_tokens).cuda()
+    r = L.greedy_accept(t, x)
+    torch.cuda.synchronize()
+    return r.n_accepted.cpu().numpy(), r.tokens.cpu().numpy(), r.argmax.cpu().numpy()
+
+
+def run_gpu_sample(case: W.Case, target_dev=None, draft_dev=None):
+    import lossless_draft_verification_amd as L
+    t = to_device(case.target) if target_dev is None else target_dev
+    d = to_device(case.draft) if draft_dev is None else draft_dev
+    x = torch.from_numpy(case.draft_tokens).cuda()
+    sd = seeds_to_device(case.seeds)
+    r = L.speculative_sample_accept(t, d, x, case.T, sd)
+    torch.cuda.synchronize()
+    return (r.n_accepted.cpu().numpy(), r.tokens.cpu().numpy(), r.p_draft.cpu().numpy(),
+            r.q_draft.cpu().numpy())

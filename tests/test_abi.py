@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The shared library must load and export every function include/specverify.h
+declares; argument validation must reject bad calls before anything is
+enqueued; the workspace size must follow the documented layout rules.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import lossless_draft_verification_amd as L
+    return L._lib
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"spec_greedy_accept", "spec_sample_accept", "spec_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_bytes_rules(lib):
+    assert lib.spec_workspace_bytes(0, 7, 1000, 1, 0) == 0
+    assert lib.spec_workspace_bytes(1, 0, 1000, 1, 0) == 0
+    assert lib.spec_workspace_bytes(1, 33, 1000, 1, 0) == 0
+    assert lib.spec_workspace_bytes(1, 7, 0, 1, 0) == 0
+    assert lib.spec_workspace_bytes(1, 7, 1000, 5, 0) == 0
+    g = lib.spec_workspace_bytes(128, 7, 262144, 1, 0)
+    s = lib.spec_workspace_bytes(128, 7, 262144, 1, 1)
+    assert g > 0 and s > g and g % 256 == 0 and s % 256 == 0
+    # grows with b and with V
+    assert lib.spec_workspace_bytes(256, 7, 262144, 1, 1) > s
+    assert lib.spec_workspace_bytes(128, 7, 2 * 262144, 1, 1) > s
+
+
+def test_status_strings(lib):
+    for code in range(0, 6):
+        assert lib.spec_status_string(code)
+
+
+def _greedy(lib, **kw):
+    a = dict(target=16, dtype=1, bs=8 * 100, rs=100, tok=16, b=2, K=7, V=100, n=16, tokens=16,
+             am=None, ws=16, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.spec_greedy_accept(a["target"], a["dtype"], a["bs"], a["rs"], a["tok"], a["b"], a["K"],
+                                  a["V"], a["n"], a["tokens"], a["am"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_greedy_argument_validation(lib):
+    # every call below is rejected on the host before any launch
+    assert _greedy(lib, target=None) == 1
+    assert _greedy(lib, tok=None) == 1
+    assert _greedy(lib, n=None) == 1
+    assert _greedy(lib, ws=None) == 1
+    assert _greedy(lib, b=0) == 1
+    assert _greedy(lib, K=0) == 1
+    assert _greedy(lib, K=33) == 1
+    assert _greedy(lib, V=0) == 1
+    assert _greedy(lib, rs=99) == 1
+    assert _greedy(lib, bs=-1) == 1
+    assert _greedy(lib, wsb=16) == 1
+    assert _greedy(lib, dtype=7) == 2
+    assert _greedy(lib, target=17) == 3      # not aligned to a bf16 element
+
+
+def _sample(lib, **kw):
+    a = dict(target=16, draft=16, dtype=1, tbs=800, trs=100, dbs=700, drs=100, tok=16, b=2, K=7, V=100,
+             T=1.0, seeds=16, n=16, tokens=16, p=None, q=None, ws=16, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.spec_sample_accept(a["target"], a["draft"], a["dtype"], a["tbs"], a["trs"], a["dbs"],
+                                  a["drs"], a["tok"], a["b"], a["K"], a["V"], a["T"], a["seeds"], a["n"],
+                                  a["tokens"], a["p"], a["q"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sample_argument_validation(lib):
+    assert _sample(lib, draft=None) == 1
+    assert _sample(lib, seeds=None) == 1
+    assert _sample(lib, T=0.0) == 1
+    assert _sample(lib, T=-1.0) == 1
+    assert _sample(lib, T=float("inf")) == 1
+    assert _sample(lib, T=float("nan")) == 1
+    assert _sample(lib, drs=50) == 1
+    assert _sample(lib, wsb=100) == 1
+    assert _sample(lib, dtype=3) == 2
+    assert _sample(lib, draft=18, dtype=0) == 3   # fp32 needs 4-byte alignment
+
+
+def test_stream_copy_validation(lib):
+    assert lib.spec_stream_copy(None, 16, 16, None) == 1
+    assert lib.spec_stream_copy(16, 16, 15, None) == 1
+    assert lib.spec_stream_copy(24, 16, 16, None) == 1
+    assert lib.spec_stream_copy(16, 32, 0, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import lossless_draft_verification_amd as L
+    t = torch.zeros(2, 8, 100, dtype=torch.bfloat16)
+    x = torch.zeros(2, 7, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        L.greedy_accept(t, x)

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case runs the same seeded bytes through both and compares element by
+element (see tests/parity.py for the near-tie accounting).  Small cases span
+several 16 KiB segments and a ragged tail; the five named workloads run at
+their full sizes, in the launch configuration the benchmark times.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import (Report, compare_greedy, compare_sample, run_gpu_greedy, run_gpu_sample,
+                    to_device, seeds_to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import lossless_draft_verification_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _check(rep: Report, name: str, max_near_tie_frac: float = 0.02):
+    rep.save(name)
+    assert not rep.failures, rep.failures[:3]
+    ties = rep.accept_near_tie_mismatch + rep.draw_near_tie_mismatch
+    assert ties <= max(1, max_near_tie_frac * max(rep.sequences, 1)), rep
+
+
+# ---------------------------------------------------------------- small cases
+
+SMALL = [
+    # name, b, K, V, dtype, kind, scale, sigma, T
+    ("bf16_ragged", 6, 3, 20000, "bf16", "normal", 2.5, (0.2, 1.5), 0.7),
+    ("f32_vec", 5, 4, 10000, "f32", "normal", 2.0, 0.5, 1.0),
+    ("f32_unaligned_rows", 4, 3, 10007, "f32", "normal", 2.0, 0.8, 0.9),
+    ("bf16_unaligned_rows", 4, 2, 1001, "bf16", "zipf", 1.0, 0.5, 1.0),
+    ("bf16_tiny_vocab", 64, 3, 8, "bf16", "normal", 1.0, 0.6, 1.0),
+    ("f32_k1", 9, 1, 3000, "f32", "normal", 3.0, 1.0, 0.5),
+    ("bf16_kmax", 3, 32, 5000, "bf16", "normal", 1.5, 0.3, 1.2),
+    ("bf16_single_seg", 7, 7, 8192, "bf16", "zipf", 1.0, 0.8, 0.8),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_greedy(spec):
+    name, b, K, V, dt, kind, scale, sig, T = spec
+    case = W.make_case(name, b=b, K=K, V=V, dtype=dt, target_kind=kind, target_scale=scale,
+                       draft_sigma=sig, rule=W.GREEDY, T=T, seed=zlib.crc32(name.encode()) % 1000)
+    _check(compare_greedy(case, *run_gpu_greedy(case), name), f"small_greedy_{name}")
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_sample(spec):
+    name, b, K, V, dt, kind, scale, sig, T = spec
+    case = W.make_case(name, b=b, K=K, V=V, dtype=dt, target_kind=kind, target_scale=scale,
+                       draft_sigma=sig, rule=W.SAMPLING, T=T, seed=zlib.crc32(name.encode()) % 1000 + 1)
+    _check(compare_sample(case, *run_gpu_sample(case), name), f"small_sample_{name}")
+
+
+def test_padded_row_stride_vector_path():
+    """V = 1001 inside rows padded to 1008 elements: 16-byte aligned rows with a
+    partial last vector."""
+    b, K, V, Vp = 5, 3, 1001, 1008
+    case = W.make_case("pad", b=b, K=K, V=V, dtype="bf16", target_scale=2.0, draft_sigma=0.7,
+                       T=0.8, seed=77)
+    tp = np.zeros((b, K + 1, Vp), np.uint16)
+    dp = np.zeros((b, K, Vp), np.uint16)
+    tp[:, :, :V] = case.target
+    dp[:, :, :V] = case.draft
+    tdev = to_device(tp)[:, :, :V]
+    ddev = to_device(dp)[:, :, :V]
+    assert tdev.stride() == ((K + 1) * Vp, Vp, 1)
+    rep = compare_greedy(case, *run_gpu_greedy(case, tdev), "pad_greedy")
+    rep.merge(compare_sample(case, *run_gpu_sample(case, tdev, ddev), "pad_sample"))
+    _check(rep, "padded_stride")
+
+
+def test_argmax_ties_lowest_index():
+    """Rounded logits produce many exact ties at the row maximum; a draft
+    token tied at a higher index is rejected."""
+    rng = np.random.default_rng(5)
+    b, K, V = 32, 5, 40000
+    z = np.round(rng.standard_normal((b, K + 1, V)) * 1.5).astype(np.float32)
+    tgt = W.bf16_bits(z)
+    zf = W.as_f32(tgt)
+    A = np.argmax(zf, axis=-1)
+    tok = A[:, :K].astype(np.int32).copy()
+    for s in range(1, b, 2):
+        j = rng.integers(K)
+        tied = np.nonzero(zf[s, j] == zf[s, j].max())[0]
+        tok[s, j] = tied[-1]
+    case = W.Case("ties", "bf16", b, K, V, 1.0, tgt, tgt[:, :K].copy(), tok,
+                  np.arange(b, dtype=np.uint64), np.zeros(b, np.int32))
+    _check(compare_greedy(case, *run_gpu_greedy(case), "ties"), "argmax_ties")
+
+
+def test_invalid_sequences():
+    case = W.make_case("inv", b=8, K=3, V=9000, dtype="bf16", target_scale=2.0, draft_sigma=0.5,
+                       T=1.0, seed=3)
+    t, d, x = case.target.copy(), case.draft.copy(), case.draft_tokens.copy()
+    t[0, 1, 100] = 0x7FC0          # NaN
+    t[1, 3, 5] = 0x7F80            # +inf
+    t[2, 2, :] = 0xFF80            # all -inf
+    d[3, 0, 8191] = 0x7FC0         # NaN in a draft row (sampling only)
+    x[4, 2] = 9000                 # token out of range
+    x[5, 0] = -7
+    t[6, 0, :4000] = 0xFF80        # masked entries only: valid
+    case = W.Case("inv", "bf16", 8, 3, 9000, 1.0, t, d, x, case.seeds, case.rule)
+    rg = compare_greedy(case, *run_gpu_greedy(case), "invalid_greedy")
+    rs = compare_sample(case, *run_gpu_sample(case), "invalid_sample")
+    n_g = run_gpu_greedy(case)[0]
+    n_s = run_gpu_sample(case)[0]
+    assert list(n_g[[0, 1, 2, 4, 5]]) == [-1] * 5 and n_g[3] >= 0 and n_g[6] >= 0
+    assert list(n_s[[0, 1, 2, 3, 4, 5]]) == [-1] * 6 and n_s[6] >= 0
+    _check(rg.merge(rs), "invalid_sequences")
+
+
+def test_draft_equal_target_all_accepted():
+    case = W.make_case("eq", b=16, K=4, V=30000, dtype="bf16", target_kind="zipf", draft_sigma=0.5,
+                       T=1.0, seed=4, equal_draft_rows=range(16))
+    n, tok, p, q = run_gpu_sample(case)
+    assert (n == case.K).all()
+    np.testing.assert_array_equal(p, q)
+    _check(compare_sample(case, n, tok, p, q, "equal"), "draft_equal_target")
+
+
+def test_deterministic_repeat():
+    case = W.make_case("det", b=12, K=7, V=50000, dtype="bf16", target_scale=3.0,
+                       draft_sigma=(0.1, 2.0), T=0.8, seed=8)
+    a = run_gpu_sample(case)
+    b = run_gpu_sample(case)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    g1, g2 = run_gpu_greedy(case), run_gpu_greedy(case)
+    for x, y in zip(g1, g2):
+        np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------------- the named workloads
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_workload_full_size(cid):
+    case = W.config(cid)
+    rep = Report()
+    if cid in (1, 2):
+        rep.merge(compare_greedy(case, *run_gpu_greedy(case), f"c{cid}_greedy"))
+    if cid in (1, 3, 4):
+        rep.merge(compare_sample(case, *run_gpu_sample(case), f"c{cid}_sample"))
+    _check(rep, f"workload_c{cid}")
+
+
+def test_workload_c5_split_calls():
+    """b=128, K=7, V=262144 bf16: rows 0..63 greedy and rows 64..127 sampling,
+    two calls on one stream over views of one [128, 8, V] block -- the
+    benchmark's launch configuration."""
+    import lossless_draft_verification_amd as L
+    case = W.config(5)
+    tdev, ddev = to_device(case.target), to_device(case.draft)
+    x = torch.from_numpy(case.draft_tokens).cuda()
+    sd = seeds_to_device(case.seeds)
+    g, s = case.rows(W.GREEDY), case.rows(W.SAMPLING)
+    g0, g1, s0, s1 = g[0], g[-1] + 1, s[0], s[-1] + 1
+    rg = L.greedy_accept(tdev[g0:g1], x[g0:g1])
+    rs = L.speculative_sample_accept(tdev[s0:s1], ddev[s0:s1], x[s0:s1], case.T, sd[s0:s1])
+    torch.cuda.synchronize()
+    rep = compare_greedy(case.take(g), rg.n_accepted.cpu().numpy(), rg.tokens.cpu().numpy(),
+                         rg.argmax.cpu().numpy(), "c5_greedy")
+    rep.merge(compare_sample(case.take(s), rs.n_accepted.cpu().numpy(), rs.tokens.cpu().numpy(),
+                             rs.p_draft.cpu().numpy(), rs.q_draft.cpu().numpy(), "c5_sample"))
+    _check(rep, "workload_c5")

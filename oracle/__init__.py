@@ -71,6 +71,9 @@ class Oracle:
         lib.oracle_sample_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32,
                                              dbl, vp, vp, vp, vp, vp, vp]
         lib.oracle_sample_accept.restype = i32
+        lib.oracle_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32,
+                                            vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_mixed_accept.restype = i32
         lib.oracle_draw_cdf.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, i32, dbl,
                                         i32, i32, i32, vp]
         lib.oracle_draw_cdf.restype = i32
@@ -151,6 +154,38 @@ class Oracle:
             "u2": diag[:, 2 * K + 2].copy(), "residual": diag[:, 2 * K + 3].copy(),
         }
 
+    def mixed_accept(self, target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
+                     temperatures: np.ndarray, seeds: np.ndarray) -> dict:
+        """Mixed batch: greedy where temperatures[s] == 0, sampling at
+        temperatures[s] > 0.  Same outputs as sample_accept plus argmax."""
+        target = np.ascontiguousarray(target)
+        draft = np.ascontiguousarray(draft)
+        x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+        temps = np.ascontiguousarray(temperatures, dtype=np.float64)
+        seeds = np.ascontiguousarray(seeds, dtype=np.uint64)
+        b, K1, V = target.shape
+        K = K1 - 1
+        assert draft.shape == (b, K, V) and draft.dtype == target.dtype
+        assert x.shape == (b, K) and seeds.shape == (b,) and temps.shape == (b,)
+        n = np.zeros(b, np.int32)
+        tok = np.zeros((b, K + 1), np.int32)
+        p = np.zeros((b, K), np.float64)
+        q = np.zeros((b, K), np.float64)
+        am = np.zeros((b, K + 1), np.int32)
+        diag = np.zeros((b, 2 * K + 4), np.float64)
+        rc = self.lib.oracle_mixed_accept(_ptr(target), _ptr(draft), _dtype_code(target),
+                                          K1 * V, V, K * V, V, _ptr(x), b, K, V, _ptr(temps),
+                                          _ptr(seeds), _ptr(n), _ptr(tok), _ptr(p), _ptr(q),
+                                          _ptr(am), _ptr(diag))
+        if rc != 0:
+            raise ValueError("oracle_mixed_accept rejected its arguments")
+        return {
+            "n_accepted": n, "tokens": tok, "p_draft": p, "q_draft": q, "argmax": am,
+            "r": diag[:, :K].copy(), "u": diag[:, K:2 * K].copy(),
+            "t": diag[:, 2 * K].copy(), "R": diag[:, 2 * K + 1].copy(),
+            "u2": diag[:, 2 * K + 2].copy(), "residual": diag[:, 2 * K + 3].copy(),
+        }
+
     def draw_cdf(self, target: np.ndarray, draft: np.ndarray, temperature: float, s: int,
                  slot: int, residual: bool) -> np.ndarray:
         """Running sums F_v of the oracle's draw weights for sequence s at `slot`."""
@@ -196,6 +231,10 @@ def greedy_accept(target, draft_tokens):
 
 def sample_accept(target, draft, draft_tokens, temperature, seeds):
     return default().sample_accept(target, draft, draft_tokens, temperature, seeds)
+
+
+def mixed_accept(target, draft, draft_tokens, temperatures, seeds):
+    return default().mixed_accept(target, draft, draft_tokens, temperatures, seeds)
 
 
 def draw_cdf(target, draft, temperature, s, slot, residual):

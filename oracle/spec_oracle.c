@@ -187,6 +187,55 @@ static double row_log_normaliser(const void *base, int dtype, int64_t off,
 /* the longest prefix with x_i == A_i; committed tokens x_0..x_{n-1}, A_n,    */
 /* then -1 up to K+1 entries.                                                */
 
+static void greedy_sequence(const void *target, int dtype,
+                            int64_t t_batch_stride, int64_t t_row_stride,
+                            const int32_t *draft_tokens, int s, int K, int V,
+                            int32_t *n_accepted, int32_t *tokens,
+                            int32_t *target_argmax)
+{
+    int valid = 1;
+    int32_t *A = (int32_t *)calloc((size_t)(K + 1), sizeof(int32_t));
+    for (int i = 0; i <= K; ++i) {
+        int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
+        if (!row_is_valid(target, dtype, off, V)) {
+            valid = 0;
+            A[i] = -1;
+        } else {
+            A[i] = row_argmax(target, dtype, off, V);
+        }
+    }
+    for (int i = 0; i < K; ++i) {
+        int32_t x = draft_tokens[(int64_t)s * K + i];
+        if (x < 0 || x >= V) {
+            valid = 0;
+        }
+    }
+    int32_t *tok = tokens + (int64_t)s * (K + 1);
+    for (int j = 0; j <= K; ++j) {
+        tok[j] = -1;
+    }
+    if (target_argmax) {
+        for (int i = 0; i <= K; ++i) {
+            target_argmax[(int64_t)s * (K + 1) + i] = valid ? A[i] : -1;
+        }
+    }
+    if (!valid) {
+        n_accepted[s] = -1;
+        free(A);
+        return;
+    }
+    int n = 0;
+    while (n < K && draft_tokens[(int64_t)s * K + n] == A[n]) {
+        ++n;
+    }
+    for (int j = 0; j < n; ++j) {
+        tok[j] = draft_tokens[(int64_t)s * K + j];
+    }
+    tok[n] = A[n];
+    n_accepted[s] = n;
+    free(A);
+}
+
 int oracle_greedy_accept(const void *target, int dtype,
                          int64_t t_batch_stride, int64_t t_row_stride,
                          const int32_t *draft_tokens, int b, int K, int V,
@@ -197,47 +246,8 @@ int oracle_greedy_accept(const void *target, int dtype,
         return 1;
     }
     for (int s = 0; s < b; ++s) {
-        int valid = 1;
-        int32_t *A = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
-        for (int i = 0; i <= K; ++i) {
-            int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
-            if (!row_is_valid(target, dtype, off, V)) {
-                valid = 0;
-                A[i] = -1;
-            } else {
-                A[i] = row_argmax(target, dtype, off, V);
-            }
-        }
-        for (int i = 0; i < K; ++i) {
-            int32_t x = draft_tokens[(int64_t)s * K + i];
-            if (x < 0 || x >= V) {
-                valid = 0;
-            }
-        }
-        int32_t *tok = tokens + (int64_t)s * (K + 1);
-        for (int j = 0; j <= K; ++j) {
-            tok[j] = -1;
-        }
-        if (target_argmax) {
-            for (int i = 0; i <= K; ++i) {
-                target_argmax[(int64_t)s * (K + 1) + i] = valid ? A[i] : -1;
-            }
-        }
-        if (!valid) {
-            n_accepted[s] = -1;
-            free(A);
-            continue;
-        }
-        int n = 0;
-        while (n < K && draft_tokens[(int64_t)s * K + n] == A[n]) {
-            ++n;
-        }
-        for (int j = 0; j < n; ++j) {
-            tok[j] = draft_tokens[(int64_t)s * K + j];
-        }
-        tok[n] = A[n];
-        n_accepted[s] = n;
-        free(A);
+        greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, V,
+                        n_accepted, tokens, target_argmax);
     }
     return 0;
 }
@@ -277,6 +287,153 @@ static double draw_weight(const void *target, const void *draft, int dtype,
  *   2K + 2        u'  = U(seed_s, s, n, 1)
  *   2K + 3        1 when the draw used the residual, 0 for p (bonus or R=0)
  */
+static void sample_sequence(const void *target, const void *draft, int dtype,
+                            int64_t t_batch_stride, int64_t t_row_stride,
+                            int64_t d_batch_stride, int64_t d_row_stride,
+                            const int32_t *draft_tokens, int s, int K, int V,
+                            double T, const uint64_t *seeds,
+                            int32_t *n_accepted, int32_t *tokens,
+                            double *p_draft, double *q_draft, double *diag)
+{
+    const int dstride = 2 * K + 4;
+    const int32_t *x = draft_tokens + (int64_t)s * K;
+    int32_t *tok = tokens + (int64_t)s * (K + 1);
+    for (int j = 0; j <= K; ++j) {
+        tok[j] = -1;
+    }
+    int valid = 1;
+    for (int i = 0; i <= K && valid; ++i) {
+        int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
+        valid = row_is_valid(target, dtype, off, V);
+    }
+    for (int i = 0; i < K && valid; ++i) {
+        int64_t off = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
+        valid = row_is_valid(draft, dtype, off, V);
+    }
+    for (int i = 0; i < K; ++i) {
+        if (x[i] < 0 || x[i] >= V) {
+            valid = 0;
+        }
+    }
+    if (!valid) {
+        n_accepted[s] = -1;
+        for (int i = 0; i < K; ++i) {
+            p_draft[(int64_t)s * K + i] = NAN;
+            q_draft[(int64_t)s * K + i] = NAN;
+        }
+        if (diag) {
+            for (int j = 0; j < dstride; ++j) {
+                diag[(int64_t)s * dstride + j] = NAN;
+            }
+        }
+        return;
+    }
+
+    /* Step 1: log-normalisers of every target and draft row. */
+    double *Ct = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    double *Cd = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int i = 0; i <= K; ++i) {
+        Ct[i] = row_log_normaliser(target, dtype,
+                                   (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride,
+                                   V, T);
+    }
+#if ORACLE_MUTANT == 5
+    const double Tq = 1.0;
+#else
+    const double Tq = T;
+#endif
+    for (int i = 0; i < K; ++i) {
+        Cd[i] = row_log_normaliser(draft, dtype,
+                                   (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride,
+                                   V, Tq);
+    }
+
+    /* Step 2: accept test of every slot, stopping the prefix at the first
+     * rejection; ratios and probabilities are reported for all K slots. */
+    int n = K;
+    for (int i = 0; i < K; ++i) {
+        int64_t toff = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
+        int64_t doff = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
+        double lp = logit_at(target, dtype, toff + x[i]) / T - Ct[i];
+        double lq = logit_at(draft, dtype, doff + x[i]) / Tq - Cd[i];
+        double p = exp(lp), q = exp(lq);
+        double r;
+        if (lp == -INFINITY) {
+            r = 0.0;               /* p(x) = 0: never accepted */
+        } else if (lq == -INFINITY) {
+            r = INFINITY;          /* q(x) = 0 < p(x): always accepted */
+        } else {
+            r = exp(lp - lq);
+        }
+        double u = oracle_uniform(seeds[s], (uint32_t)s, (uint32_t)i, 0u);
+        p_draft[(int64_t)s * K + i] = p;
+        q_draft[(int64_t)s * K + i] = q;
+        if (diag) {
+            diag[(int64_t)s * dstride + i] = r;
+            diag[(int64_t)s * dstride + K + i] = u;
+        }
+        double accept_prob = r < 1.0 ? r : 1.0;
+        if (n == K && !(u < accept_prob)) {
+            n = i;
+        }
+    }
+
+    /* Step 3: draw the token at slot n: residual when n < K, bonus from
+     * p_{K+1} when n == K; inverse CDF in ascending vocabulary order. */
+#if ORACLE_MUTANT == 3
+    const int draw_row = n < K ? n : K - 1;
+#else
+    const int draw_row = n;
+#endif
+    int64_t toff = (int64_t)s * t_batch_stride + (int64_t)draw_row * t_row_stride;
+    int64_t doff = (int64_t)s * d_batch_stride + (int64_t)(n < K ? n : 0) * d_row_stride;
+    int residual = n < K;
+    double Cdn = residual ? Cd[n] : 0.0;
+    double R = 0.0;
+    for (int v = 0; v < V; ++v) {
+        R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
+    }
+    if (residual && R == 0.0) {
+        residual = 0;              /* no residual mass: draw from p_n */
+        R = 0.0;
+        for (int v = 0; v < V; ++v) {
+            R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, 0);
+        }
+    }
+    double u2 = oracle_uniform(seeds[s], (uint32_t)s, (uint32_t)n, 1u);
+    double t = u2 * R;
+    int32_t y = -1, last_positive = -1;
+    double F = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double w = draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
+        F += w;
+        if (w > 0.0) {
+            last_positive = v;
+        }
+        if (F > t) {
+            y = v;
+            break;
+        }
+    }
+    if (y < 0) {
+        y = last_positive;         /* t at the top end by rounding */
+    }
+
+    for (int j = 0; j < n; ++j) {
+        tok[j] = x[j];
+    }
+    tok[n] = y;
+    n_accepted[s] = n;
+    if (diag) {
+        diag[(int64_t)s * dstride + 2 * K] = t;
+        diag[(int64_t)s * dstride + 2 * K + 1] = R;
+        diag[(int64_t)s * dstride + 2 * K + 2] = u2;
+        diag[(int64_t)s * dstride + 2 * K + 3] = residual ? 1.0 : 0.0;
+    }
+    free(Ct);
+    free(Cd);
+}
+
 int oracle_sample_accept(const void *target, const void *draft, int dtype,
                          int64_t t_batch_stride, int64_t t_row_stride,
                          int64_t d_batch_stride, int64_t d_row_stride,
@@ -289,29 +446,53 @@ int oracle_sample_accept(const void *target, const void *draft, int dtype,
         (dtype != OR_F32 && dtype != OR_BF16)) {
         return 1;
     }
+    for (int s = 0; s < b; ++s) {
+        sample_sequence(target, draft, dtype, t_batch_stride, t_row_stride,
+                        d_batch_stride, d_row_stride, draft_tokens, s, K, V, T, seeds,
+                        n_accepted, tokens, p_draft, q_draft, diag);
+    }
+    return 0;
+}
+
+/* Mixed batch: sequence s follows the greedy rule when temps[s] == 0 and the
+ * sampling rule at temperature temps[s] when temps[s] > 0 is finite (the
+ * drafter's temperature 0.0 stands for greedy decoding, "dspark-mlx 0.1.0",
+ * dspark_mlx/arch/gemma4.py, Gemma4DSparkArgs); any other value makes the
+ * sequence invalid.  Each sequence gets exactly what the single-rule
+ * functions compute for it, with its index s in this batch as the Philox
+ * row.  Greedy sequences report NaN probabilities; sampling sequences report
+ * -1 argmax entries. */
+int oracle_mixed_accept(const void *target, const void *draft, int dtype,
+                        int64_t t_batch_stride, int64_t t_row_stride,
+                        int64_t d_batch_stride, int64_t d_row_stride,
+                        const int32_t *draft_tokens, int b, int K, int V,
+                        const double *temps, const uint64_t *seeds,
+                        int32_t *n_accepted, int32_t *tokens,
+                        double *p_draft, double *q_draft, int32_t *target_argmax,
+                        double *diag)
+{
+    if (b < 1 || K < 1 || V < 1 || (dtype != OR_F32 && dtype != OR_BF16)) {
+        return 1;
+    }
     const int dstride = 2 * K + 4;
     for (int s = 0; s < b; ++s) {
-        const int32_t *x = draft_tokens + (int64_t)s * K;
-        int32_t *tok = tokens + (int64_t)s * (K + 1);
-        for (int j = 0; j <= K; ++j) {
-            tok[j] = -1;
-        }
-        int valid = 1;
-        for (int i = 0; i <= K && valid; ++i) {
-            int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
-            valid = row_is_valid(target, dtype, off, V);
-        }
-        for (int i = 0; i < K && valid; ++i) {
-            int64_t off = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
-            valid = row_is_valid(draft, dtype, off, V);
-        }
-        for (int i = 0; i < K; ++i) {
-            if (x[i] < 0 || x[i] >= V) {
-                valid = 0;
+        const double T = temps[s];
+        const int greedy = T == 0.0;
+        const int sampling = T > 0.0 && !isinf(T);
+        if (greedy) {
+            greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, V,
+                            n_accepted, tokens, target_argmax);
+        } else if (sampling) {
+            sample_sequence(target, draft, dtype, t_batch_stride, t_row_stride,
+                            d_batch_stride, d_row_stride, draft_tokens, s, K, V, T, seeds,
+                            n_accepted, tokens, p_draft, q_draft, diag);
+        } else {
+            n_accepted[s] = -1;
+            for (int j = 0; j <= K; ++j) {
+                tokens[(int64_t)s * (K + 1) + j] = -1;
             }
         }
-        if (!valid) {
-            n_accepted[s] = -1;
+        if (!sampling) {
             for (int i = 0; i < K; ++i) {
                 p_draft[(int64_t)s * K + i] = NAN;
                 q_draft[(int64_t)s * K + i] = NAN;
@@ -321,112 +502,12 @@ int oracle_sample_accept(const void *target, const void *draft, int dtype,
                     diag[(int64_t)s * dstride + j] = NAN;
                 }
             }
-            continue;
         }
-
-        /* Step 1: log-normalisers of every target and draft row. */
-        double *Ct = (double *)malloc(sizeof(double) * (size_t)(K + 1));
-        double *Cd = (double *)malloc(sizeof(double) * (size_t)K);
-        for (int i = 0; i <= K; ++i) {
-            Ct[i] = row_log_normaliser(target, dtype,
-                                       (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride,
-                                       V, T);
-        }
-#if ORACLE_MUTANT == 5
-        const double Tq = 1.0;
-#else
-        const double Tq = T;
-#endif
-        for (int i = 0; i < K; ++i) {
-            Cd[i] = row_log_normaliser(draft, dtype,
-                                       (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride,
-                                       V, Tq);
-        }
-
-        /* Step 2: accept test of every slot, stopping the prefix at the first
-         * rejection; ratios and probabilities are reported for all K slots. */
-        int n = K;
-        for (int i = 0; i < K; ++i) {
-            int64_t toff = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
-            int64_t doff = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
-            double lp = logit_at(target, dtype, toff + x[i]) / T - Ct[i];
-            double lq = logit_at(draft, dtype, doff + x[i]) / Tq - Cd[i];
-            double p = exp(lp), q = exp(lq);
-            double r;
-            if (lp == -INFINITY) {
-                r = 0.0;               /* p(x) = 0: never accepted */
-            } else if (lq == -INFINITY) {
-                r = INFINITY;          /* q(x) = 0 < p(x): always accepted */
-            } else {
-                r = exp(lp - lq);
-            }
-            double u = oracle_uniform(seeds[s], (uint32_t)s, (uint32_t)i, 0u);
-            p_draft[(int64_t)s * K + i] = p;
-            q_draft[(int64_t)s * K + i] = q;
-            if (diag) {
-                diag[(int64_t)s * dstride + i] = r;
-                diag[(int64_t)s * dstride + K + i] = u;
-            }
-            double accept_prob = r < 1.0 ? r : 1.0;
-            if (n == K && !(u < accept_prob)) {
-                n = i;
+        if (!greedy && target_argmax) {
+            for (int i = 0; i <= K; ++i) {
+                target_argmax[(int64_t)s * (K + 1) + i] = -1;
             }
         }
-
-        /* Step 3: draw the token at slot n: residual when n < K, bonus from
-         * p_{K+1} when n == K; inverse CDF in ascending vocabulary order. */
-#if ORACLE_MUTANT == 3
-        const int draw_row = n < K ? n : K - 1;
-#else
-        const int draw_row = n;
-#endif
-        int64_t toff = (int64_t)s * t_batch_stride + (int64_t)draw_row * t_row_stride;
-        int64_t doff = (int64_t)s * d_batch_stride + (int64_t)(n < K ? n : 0) * d_row_stride;
-        int residual = n < K;
-        double Cdn = residual ? Cd[n] : 0.0;
-        double R = 0.0;
-        for (int v = 0; v < V; ++v) {
-            R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
-        }
-        if (residual && R == 0.0) {
-            residual = 0;              /* no residual mass: draw from p_n */
-            R = 0.0;
-            for (int v = 0; v < V; ++v) {
-                R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, 0);
-            }
-        }
-        double u2 = oracle_uniform(seeds[s], (uint32_t)s, (uint32_t)n, 1u);
-        double t = u2 * R;
-        int32_t y = -1, last_positive = -1;
-        double F = 0.0;
-        for (int v = 0; v < V; ++v) {
-            double w = draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
-            F += w;
-            if (w > 0.0) {
-                last_positive = v;
-            }
-            if (F > t) {
-                y = v;
-                break;
-            }
-        }
-        if (y < 0) {
-            y = last_positive;         /* t at the top end by rounding */
-        }
-
-        for (int j = 0; j < n; ++j) {
-            tok[j] = x[j];
-        }
-        tok[n] = y;
-        n_accepted[s] = n;
-        if (diag) {
-            diag[(int64_t)s * dstride + 2 * K] = t;
-            diag[(int64_t)s * dstride + 2 * K + 1] = R;
-            diag[(int64_t)s * dstride + 2 * K + 2] = u2;
-            diag[(int64_t)s * dstride + 2 * K + 3] = residual ? 1.0 : 0.0;
-        }
-        free(Ct);
-        free(Cd);
     }
     return 0;
 }

@@ -227,3 +227,28 @@ def test_invalid_inputs(orc):
         orc.sample_accept(t, d, x, 0.0, case.seeds)
     with pytest.raises(ValueError):
         orc.sample_accept(t, d, x, float("inf"), case.seeds)
+
+
+def test_mixed_batch_is_per_sequence_dispatch(orc):
+    """A mixed batch (temperature 0 = greedy, else sampling) gives every
+    sequence what the single-rule oracle gives it at the same batch index;
+    a negative or non-finite temperature invalidates only its sequence."""
+    case = W.make_case("mix", b=10, K=3, V=2000, dtype="bf16", target_scale=2.0,
+                       draft_sigma=0.6, T=0.8, seed=21)
+    temps = np.array([0.0, 0.8] * 5)
+    temps[9] = -1.0
+    res = orc.mixed_accept(case.target, case.draft, case.draft_tokens, temps, case.seeds)
+    n_g, tok_g, am_g = orc.greedy_accept(case.target, case.draft_tokens)
+    smp = orc.sample_accept(case.target, case.draft, case.draft_tokens, 0.8, case.seeds)
+    for s in range(10):
+        if s == 9:
+            assert res["n_accepted"][s] == -1 and (res["tokens"][s] == -1).all()
+        elif temps[s] == 0.0:
+            assert res["n_accepted"][s] == n_g[s]
+            assert (res["tokens"][s] == tok_g[s]).all() and (res["argmax"][s] == am_g[s]).all()
+            assert np.isnan(res["p_draft"][s]).all()
+        else:
+            assert res["n_accepted"][s] == smp["n_accepted"][s]
+            assert (res["tokens"][s] == smp["tokens"][s]).all()
+            assert (res["p_draft"][s] == smp["p_draft"][s]).all()
+            assert (res["argmax"][s] == -1).all()

@@ -1,18 +1,24 @@
 """Benchmark of the verify/accept step on one MI355X.
 
 One step = one verify pass over the workload b=128, K=7, V=262144, bf16
-logits, T=0.8: a greedy-accept call over sequences 0..63 and a
-speculative-sampling call over sequences 64..127, back to back on one stream
-(target block [128, 8, V], draft block [128, 7, V], all resident in HBM).
-Inputs rotate over several device copies so no step reads bytes a previous
-step left in the 256 MB last-level cache.
+logits: sequences 0..63 greedy, 64..127 speculative sampling at T=0.8
+(target block [128, 8, V], draft block [128, 7, V], draft tokens, seeds,
+all resident in HBM).  By default the step is ONE mixed-rule call
+(spec_mixed_accept, per-sequence temperature 0 or 0.8); `--step split` runs
+it as a greedy call over 0..63 plus a sampling call over 64..127 on the same
+stream.  Inputs rotate over several device copies so no step reads bytes a
+previous step left in the 256 MB last-level cache.
 
-Prints one JSON line: verify blocks/s (whole job), the row pass's achieved
-HBM bandwidth against the 8 TB/s peak (kernel time from HIP events recorded
-on the call's stream by the library's stage hook), and the CPU oracle timed on
-a bounded sample of the same workload on the host.
+Timed regions (HIP events on the call stream, synchronised on both sides):
+  1. `--steps` steps, nothing else recorded: the headline value;
+  2. the same steps with the library's stage events recorded around every
+     kernel: per-kernel times and the row pass's achieved HBM bandwidth;
+  3. (mixed) the same steps as split calls, for reference.
+Then the CPU oracle is timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+Prints one JSON line.  Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--step mixed|split]
+  python bench.py --copy-calibration BYTES   (rocprof counter calibration)
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SEG_BYTES = 16384          # one row-pass segment (the bonus draw re-reads one)
 
 
 def log(msg: str) -> None:
@@ -51,8 +58,8 @@ def source_digest() -> str:
 
 
 def load_traffic(kernel: str, workload: str):
-    """Bytes per launch from committed rocprofv3 --pmc summaries, valid only
-    while the kernel source is unchanged since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, valid
+    only while the kernel source is unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -68,14 +75,13 @@ def load_traffic(kernel: str, workload: str):
 def cpu_baseline(case, greedy_idx, sample_idx, budget_s: float):
     """Time the CPU oracle (single thread) on whole sequences of the workload,
     alternating greedy and sampling sequences until the budget is spent."""
-    import numpy as np
     import oracle
     orc = oracle.default()
     tg = ts = 0.0
     ng = ns = 0
     t_begin = time.perf_counter()
     k = 0
-    while (time.perf_counter() - t_begin < budget_s and k < len(greedy_idx)) or k == 0:
+    while k == 0 or (time.perf_counter() - t_begin < budget_s and k < min(len(greedy_idx), len(sample_idx))):
         g = case.take([greedy_idx[k]])
         t0 = time.perf_counter()
         orc.greedy_accept(g.target, g.draft_tokens)
@@ -90,28 +96,139 @@ def cpu_baseline(case, greedy_idx, sample_idx, budget_s: float):
     per_block = 0.5 * (tg / ng) + 0.5 * (ts / ns)
     return {
         "value": 1.0 / per_block, "unit": "verify blocks/s", "cores": 1, "kind": "oracle",
-        "sample": f"{ng} greedy + {ns} sampling sequences of the same workload "
-                  f"(whole sequences, single-threaded C oracle in double precision, gcc -O2); "
-                  f"greedy {tg / ng * 1e3:.1f} ms/seq, sampling {ts / ns * 1e3:.1f} ms/seq; "
+        "sample": f"{ng} greedy + {ns} sampling sequences of the same workload, whole sequences, "
+                  f"mixed 50/50 as in the workload (single-threaded C oracle in double precision, "
+                  f"gcc -O2): greedy {tg / ng * 1e3:.1f} ms/seq, sampling {ts / ns * 1e3:.1f} ms/seq; "
                   f"host CPU: {cpu_model()}, {os.cpu_count()} logical CPUs visible",
     }
+
+
+KERNEL_KEYS = {"row_pass": "row_pass", "scan_kernel": "scan", "residual_kernel": "residual_mass",
+               "draw_kernel": "draw_token", "stream_copy_kernel": "stream_copy"}
+
+
+def _short(name: str) -> str:
+    for k, v in KERNEL_KEYS.items():
+        if k in name:
+            return v
+    return name.split("(")[0][-40:]
+
+
+def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 536870912) -> int:
+    """Turn rocprofv3 CSV output (a kernel trace and --pmc FETCH_SIZE /
+    WRITE_SIZE passes over the bench and over --copy-calibration, written
+    under `rdir` by the commands listed in the summary) into
+    profiles/verify_c5_mixed.md and profiles/traffic.json."""
+    import csv
+    import statistics
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    tr = os.path.join(rdir, "prof", "mixed_c5_kernel_trace.csv")
+    rows = list(csv.DictReader(open(tr)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = {}
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counter(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            out.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return out
+
+    pmc = os.path.join(rdir, "pmc")
+    fb, wb = (counter(os.path.join(pmc, f"bench_{c}_counter_collection.csv")) for c in ("FETCH_SIZE", "WRITE_SIZE"))
+    fc, wc = (counter(os.path.join(pmc, f"copy_{c}_counter_collection.csv")) for c in ("FETCH_SIZE", "WRITE_SIZE"))
+    kib = nbytes_copy / 1024.0
+    f_scale = kib / statistics.median(fc["stream_copy"])
+    w_scale = kib / statistics.median(wc["stream_copy"])
+    digest = source_digest()
+    lines = ["# Kernel durations and HBM traffic: verify step, workload c5 (mixed call)", "",
+             "b=128, K=7, V=262144, bf16; sequences 0..63 greedy, 64..127 sampling at T=0.8, one",
+             "spec_mixed_accept call per step.  Kernel source sha256[:16] = `%s`." % digest, "",
+             "Commands (run from /tmp, repository at $R, rocprofv3 output under $OUT):", "",
+             "    rocprofv3 --kernel-trace --stats -d $OUT/prof -o mixed_c5 --output-format csv \\",
+             "        -- python3 $R/bench.py --steps 200 --warmup 1000 --no-cpu-baseline --no-reference",
+             "    rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc -o bench_FETCH_SIZE --output-format csv \\",
+             "        -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-reference",
+             "    rocprofv3 --pmc WRITE_SIZE  (same, -o bench_WRITE_SIZE)",
+             "    rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc -o copy_FETCH_SIZE --output-format csv \\",
+             "        -- python3 $R/bench.py --copy-calibration %d" % nbytes_copy,
+             "    rocprofv3 --pmc WRITE_SIZE  (same, -o copy_WRITE_SIZE)",
+             "    python bench.py --summarize-rocprof $OUT            # writes this file", "",
+             "## Kernel trace (rocprofv3 --kernel-trace), last 200 steps", "",
+             "| kernel | launches | median us | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for k, v in dur.items():
+        if k not in KERNEL_KEYS.values():
+            continue
+        v = v[-200:]
+        lines.append(f"| {k} | {len(v)} | {statistics.median(v):.2f} | {statistics.mean(v):.2f} | "
+                     f"{min(v):.2f} | {max(v):.2f} |")
+    lines += ["", "## Counters (rocprofv3 --pmc, one counter per run), KiB per dispatch", "",
+              f"Calibration: spec_stream_copy of {nbytes_copy} bytes reads FETCH_SIZE "
+              f"{statistics.median(fc['stream_copy']):.0f} KiB and WRITE_SIZE "
+              f"{statistics.median(wc['stream_copy']):.0f} KiB for {kib:.0f} KiB moved each way, so "
+              f"FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.", "",
+              "| kernel | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) | HBM bytes per launch (scaled) |",
+              "|---|---|---|---|"]
+    traffic = {}
+    for k in fb:
+        if k not in ("row_pass", "scan", "residual_mass", "draw_token"):
+            continue
+        f_med, w_med = statistics.median(fb[k]), statistics.median(wb.get(k, [0.0]))
+        byts = (f_med * f_scale + w_med * w_scale) * 1024.0
+        traffic[k] = {workload: {"bytes_per_launch": byts, "fetch_kib": f_med, "write_kib": w_med,
+                                 "fetch_scale": f_scale, "write_scale": w_scale, "source_sha256_16": digest}}
+        lines.append(f"| {k} | {f_med:.0f} | {w_med:.0f} | {byts:.0f} |")
+    lines += ["", "Algorithmic bytes of the row pass per launch: 771751936 (every logit read once).", ""]
+    with open(os.path.join(prof, "verify_c5_mixed.md"), "w") as f:
+        f.write("\n".join(lines))
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print("\n".join(lines))
+    return 0
+
+
+def copy_calibration(nbytes: int) -> int:
+    import torch
+    import lossless_draft_verification_amd as L
+    dev = torch.device("cuda:0")
+    src = torch.full((nbytes // 4,), 1.0, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        L.stream_copy(dst, src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5,
+                      "expected_fetch_bytes": nbytes, "expected_write_bytes": nbytes}), flush=True)
+    return 0
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first; about 1000 (0.15 s) lets the GPU clocks settle")
     ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--step", choices=["mixed", "split"], default="mixed")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true", help="skip the split-call reference region")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--summarize-rocprof", default="", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 CSVs under DIR and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        return summarize_rocprof(args.summarize_rocprof)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the verify step shards by sequence with no exchange; see the design notes).",
               file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
 
     import numpy as np
     import torch
@@ -127,43 +244,52 @@ def main() -> int:
     t0 = time.time()
     case = W.config(args.workload)
     log(f"generated in {time.time() - t0:.1f}s")
-    gidx, sidx = case.rows(W.GREEDY), case.rows(W.SAMPLING)
+    K, V, b = case.K, case.V, case.b
     if args.workload == 1:
-        gidx = sidx = np.arange(case.b)          # both rules on the same sequence
+        temps_np = np.full(b, case.T)                # one sequence: sampling rule
+    else:
+        temps_np = np.where(case.rule == W.GREEDY, 0.0, case.T)
+    gidx, sidx = np.nonzero(temps_np == 0.0)[0], np.nonzero(temps_np > 0.0)[0]
     has_g, has_s = len(gidx) > 0, len(sidx) > 0
-    if has_g and args.workload != 1:
-        assert (np.diff(gidx) == 1).all()
-    if has_s and args.workload != 1:
-        assert (np.diff(sidx) == 1).all()
+    for idx in (gidx, sidx):
+        assert len(idx) == 0 or (np.diff(idx) == 1).all(), "each rule must own a contiguous range"
 
     def to_dev(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    tgt0 = to_dev(case.target)
-    drf0 = to_dev(case.draft)
+    tgt0, drf0 = to_dev(case.target), to_dev(case.draft)
     copies = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(args.copies - 1)]
     x = torch.from_numpy(case.draft_tokens).to(dev)
     seeds = torch.from_numpy(case.seeds.view(np.int64)).to(dev)
-    K, V, b = case.K, case.V, case.b
+    temps = torch.from_numpy(temps_np.astype(np.float64)).to(dev)
+    dt = tgt0.dtype
     g0, g1 = (int(gidx[0]), int(gidx[-1]) + 1) if has_g else (0, 0)
     s0, s1 = (int(sidx[0]), int(sidx[-1]) + 1) if has_s else (0, 0)
     bg, bs = g1 - g0, s1 - s0
-    out_g = L.AcceptResult(torch.empty(bg, dtype=torch.int32, device=dev),
-                           torch.empty(bg, K + 1, dtype=torch.int32, device=dev),
-                           argmax=torch.empty(bg, K + 1, dtype=torch.int32, device=dev)) if has_g else None
-    out_s = L.AcceptResult(torch.empty(bs, dtype=torch.int32, device=dev),
-                           torch.empty(bs, K + 1, dtype=torch.int32, device=dev),
-                           p_draft=torch.empty(bs, K, dtype=torch.float32, device=dev),
-                           q_draft=torch.empty(bs, K, dtype=torch.float32, device=dev)) if has_s else None
-    ws_g = torch.empty(L.workspace_bytes(bg, K, V, tgt0.dtype, False) if has_g else 1, dtype=torch.uint8,
-                       device=dev)
-    ws_s = torch.empty(L.workspace_bytes(bs, K, V, tgt0.dtype, True) if has_s else 1, dtype=torch.uint8,
-                       device=dev)
+
+    def res(n, samp, greedy):
+        return L.AcceptResult(torch.empty(n, dtype=torch.int32, device=dev),
+                              torch.empty(n, K + 1, dtype=torch.int32, device=dev),
+                              p_draft=torch.empty(n, K, device=dev) if samp else None,
+                              q_draft=torch.empty(n, K, device=dev) if samp else None,
+                              argmax=torch.empty(n, K + 1, dtype=torch.int32, device=dev) if greedy else None)
+
+    out_m = res(b, True, True)
+    ws_m = torch.zeros(L.mixed_workspace_bytes(b, K, V, dt), dtype=torch.uint8, device=dev)
+    out_g = res(max(bg, 1), False, True)
+    ws_g = torch.zeros(L.workspace_bytes(max(bg, 1), K, V, dt, False), dtype=torch.uint8, device=dev)
+    out_s = res(max(bs, 1), True, False)
+    ws_s = torch.zeros(L.workspace_bytes(max(bs, 1), K, V, dt, True), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(k, gev=None, sev=None):
+    def step_mixed(k, evs=None):
+        t, d = copies[k % len(copies)]
+        L.set_stage_events(evs)
+        L.mixed_accept(t, d, x, temps, seeds, out=out_m, workspace=ws_m, stream=stream)
+
+    def step_split(k, gev=None, sev=None):
         t, d = copies[k % len(copies)]
         if has_g:
             L.set_stage_events(gev)
@@ -179,54 +305,80 @@ def main() -> int:
             e.record(stream)          # creates the underlying hipEvent
         return evs
 
-    log(f"warmup {args.warmup} steps")
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    L.set_stage_events(None)
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(n):
+            fn(k)
+        end.record(stream)
+        torch.cuda.synchronize()
+        L.set_stage_events(None)
+        return start.elapsed_time(end)
 
-    gevs = [mk_events(3) for _ in range(args.steps)] if has_g else [None] * args.steps
-    sevs = [mk_events(5) for _ in range(args.steps)] if has_s else [None] * args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mixed = args.step == "mixed"
+    main_step = (lambda k: step_mixed(k)) if mixed else (lambda k: step_split(k))
+    log(f"warmup {args.warmup} steps ({args.step})")
+    for k in range(args.warmup):
+        main_step(k)
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    start.record(stream)
-    for k in range(args.steps):
-        step(k, gevs[k], sevs[k])
-    end.record(stream)
-    torch.cuda.synchronize()
-    L.set_stage_events(None)
-    total_ms = start.elapsed_time(end)
+
+    log(f"region 1: {args.steps} timed steps")
+    total_ms = timed(main_step, args.steps)
     ms_per_step = total_ms / args.steps
     blocks_per_s = b * args.steps / (total_ms * 1e-3)
 
-    es = 2 if tgt0.dtype == torch.bfloat16 else 4
+    log("region 2: the same steps with stage events")
     stage = {}
-    if has_g:
-        stage["row_stats_greedy"] = float(np.mean([gevs[k][0].elapsed_time(gevs[k][1]) for k in range(args.steps)]))
-        stage["scan_greedy"] = float(np.mean([gevs[k][1].elapsed_time(gevs[k][2]) for k in range(args.steps)]))
-    if has_s:
-        names = ["row_stats_sample", "scan_sample", "residual_mass", "draw_token"]
+    names = ["row_pass", "scan", "residual_mass", "draw_token"]
+    if mixed:
+        evs = [mk_events(5) for _ in range(args.steps)]
+        staged_ms = timed(lambda k: step_mixed(k, evs[k]), args.steps)
         for j, nm in enumerate(names):
-            stage[nm] = float(np.mean([sevs[k][j].elapsed_time(sevs[k][j + 1]) for k in range(args.steps)]))
+            stage[nm] = float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
+    else:
+        gevs = [mk_events(3) for _ in range(args.steps)] if has_g else [None] * args.steps
+        sevs = [mk_events(5) for _ in range(args.steps)] if has_s else [None] * args.steps
+        staged_ms = timed(lambda k: step_split(k, gevs[k], sevs[k]), args.steps)
+        if has_g:
+            for j, nm in enumerate(names[:2]):
+                stage["greedy_" + nm] = float(np.mean([gevs[k][j].elapsed_time(gevs[k][j + 1])
+                                                       for k in range(args.steps)]))
+        if has_s:
+            for j, nm in enumerate(names):
+                stage["sample_" + nm] = float(np.mean([sevs[k][j].elapsed_time(sevs[k][j + 1])
+                                                       for k in range(args.steps)]))
+
+    reference = None
+    if mixed and not args.no_reference and has_g and has_s:
+        log("region 3: the same steps as two split calls (reference)")
+        for k in range(min(args.warmup, 100)):
+            step_split(k)
+        ref_ms = timed(lambda k: step_split(k), args.steps) / args.steps
+        reference = {"split_calls_ms_per_step": ref_ms, "split_calls_blocks_per_s": b / (ref_ms * 1e-3)}
 
     # outcome of the (identical) steps, for the algorithmic byte count
-    n_s = out_s.n_accepted.cpu().numpy() if has_s else np.zeros(0)
+    if mixed:
+        n_all = out_m.n_accepted.cpu().numpy()
+        n_s = n_all[sidx] if has_s else np.zeros(0, np.int32)
+    else:
+        n_s = out_s.n_accepted.cpu().numpy()[:bs] if has_s else np.zeros(0, np.int32)
     rejected = int(((n_s >= 0) & (n_s < K)).sum())
     bonus = int((n_s == K).sum())
-    seg_bytes = 16384
+    es = 2 if dt == torch.bfloat16 else 4
     bytes_greedy = bg * (K + 1) * V * es
     bytes_sample_pass = bs * (2 * K + 1) * V * es
-    # per sampling sequence: one pass over 2K+1 rows, plus the rejected row
-    # pair read again for the residual, or one segment of the bonus row
-    bytes_step = bytes_greedy + bytes_sample_pass + rejected * 2 * V * es + bonus * seg_bytes
-    if has_s:
-        dom, dom_bytes = "row_stats_sample", bytes_sample_pass
+    # per sampling sequence: one pass over its 2K+1 rows, plus the rejected
+    # row pair read again for the residual, or one segment of the bonus row
+    bytes_step = bytes_greedy + bytes_sample_pass + rejected * 2 * V * es + bonus * SEG_BYTES
+    if mixed:
+        dom, dom_bytes, dom_ms = "row_pass", bytes_greedy + bytes_sample_pass, stage["row_pass"]
+    elif has_s:
+        dom, dom_bytes, dom_ms = "row_pass", bytes_sample_pass, stage["sample_row_pass"]
     else:
-        dom, dom_bytes = "row_stats_greedy", bytes_greedy
-    dom_ms = stage[dom]
+        dom, dom_bytes, dom_ms = "row_pass", bytes_greedy, stage["greedy_row_pass"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(dom, f"c{args.workload}")
+    traffic = load_traffic(dom, f"c{args.workload}_{args.step}")
 
     result = {
         "metric": "verify blocks/s and achieved HBM GB/s (% of peak), b=128 K=7 V=262144 bf16",
@@ -245,6 +397,9 @@ def main() -> int:
             "workload": f"c{args.workload}: {W.CONFIG_TEXT[args.workload]}",
             "b": b, "K": K, "V": V, "temperature": case.T,
             "greedy_sequences": bg, "sampling_sequences": bs,
+            "step": ("one spec_mixed_accept call (per-sequence temperature 0 / 0.8)" if mixed else
+                     "spec_greedy_accept over the greedy sequences + spec_sample_accept over the "
+                     "sampling sequences, one stream"),
             "input_copies_rotated": len(copies),
             "parallelism": "single GPU",
         },
@@ -266,6 +421,8 @@ def main() -> int:
             "rejected_sequences": rejected, "bonus_sequences": bonus,
         },
         "stage_ms": stage,
+        "staged_ms_per_step": staged_ms / args.steps,
+        "reference": reference,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -126,12 +126,42 @@ int spec_sample_accept(const void *target, const void *draft, int dtype,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * Mixed batch: each sequence picks its rule by its own temperature, as a
+ * serving batch mixes greedy and sampled requests.  temperatures[s] == 0
+ * selects the greedy rule for sequence s (the drafter's temperature 0.0
+ * default meaning greedy decoding, "dspark-mlx 0.1.0" wheel diff,
+ * dspark_mlx/arch/gemma4.py, Gemma4DSparkArgs); a finite temperatures[s] > 0
+ * selects the sampling rule at that temperature; any other value makes the
+ * sequence invalid (n_accepted = -1).  Every sequence gets exactly what
+ * spec_greedy_accept / spec_sample_accept give it, with its index s in THIS
+ * batch as the Philox row.  Draft rows of greedy sequences are never read.
+ *
+ *   temperatures    [b] double (device)
+ *   p_draft, q_draft  [b, K] float out or NULL (NaN for greedy sequences)
+ *   target_argmax   [b, K+1] int32 out or NULL (-1 for sampling sequences)
+ *   workspace       spec_mixed_workspace_bytes(b, K, V, dtype) bytes (device)
+ * Other arguments as for spec_sample_accept.  Four kernels, like the
+ * sampling rule alone.
+ */
+size_t spec_mixed_workspace_bytes(int b, int K, int V, int dtype);
+
+int spec_mixed_accept(const void *target, const void *draft, int dtype,
+                      int64_t t_batch_stride, int64_t t_row_stride,
+                      int64_t d_batch_stride, int64_t d_row_stride,
+                      const int32_t *draft_tokens, int b, int K, int V,
+                      const double *temperatures, const uint64_t *seeds,
+                      int32_t *n_accepted, int32_t *tokens,
+                      float *p_draft, float *q_draft, int32_t *target_argmax,
+                      void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Profiling hook (not part of the accept semantics).  Registers, for the
  * calling host thread only, an array of n_events hipEvent_t handles.  While
  * registered, each accept call records events[0] before its first kernel and
- * events[k] after its k-th kernel (k = 1 .. number of kernels, 2 for greedy,
- * 4 for sampling) on its stream, if n_events is large enough; otherwise it
- * records nothing.  Pass NULL / 0 to unregister.  Returns SPEC_OK.
+ * events[k] after its k-th kernel on its stream (kernels: 1 row pass, 2 scan,
+ * then for sampling and mixed calls 3 residual pass, 4 draw), for every
+ * k < n_events; n_events = 2 brackets the row pass alone.  Pass NULL / 0 to
+ * unregister.  Returns SPEC_OK.
  */
 int spec_set_stage_events(void *const *events, int n_events);
 

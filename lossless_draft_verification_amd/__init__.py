@@ -23,7 +23,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "workspace_bytes",
+__all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_accept",
+           "workspace_bytes", "mixed_workspace_bytes",
            "set_stage_events", "stream_copy", "library_path", "SpecError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,11 @@ def _load():
     lib.spec_sample_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, dbl, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
     lib.spec_sample_accept.restype = i32
+    lib.spec_mixed_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_mixed_workspace_bytes.restype = sz
+    lib.spec_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_mixed_accept.restype = i32
     lib.spec_set_stage_events.argtypes = [vp, i32]
     lib.spec_set_stage_events.restype = i32
     lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
@@ -113,6 +119,14 @@ class AcceptResult:
 def workspace_bytes(b: int, K: int, V: int, dtype: torch.dtype, sampling: bool) -> int:
     code = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
     n = _lib.spec_workspace_bytes(b, K, V, code, int(bool(sampling)))
+    if n == 0:
+        raise ValueError(f"sizes out of range: b={b} K={K} V={V}")
+    return n
+
+
+def mixed_workspace_bytes(b: int, K: int, V: int, dtype: torch.dtype) -> int:
+    code = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
+    n = _lib.spec_mixed_workspace_bytes(b, K, V, code)
     if n == 0:
         raise ValueError(f"sizes out of range: b={b} K={K} V={V}")
     return n
@@ -188,6 +202,46 @@ def speculative_sample_accept(target: torch.Tensor, draft: torch.Tensor, draft_t
         seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
         out.p_draft.data_ptr() if out.p_draft is not None else None,
         out.q_draft.data_ptr() if out.q_draft is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                 temperatures: torch.Tensor, seeds: torch.Tensor, *, out: Optional[AcceptResult] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> AcceptResult:
+    """Mixed batch: sequence s is greedy when temperatures[s] == 0 and sampled
+    at temperatures[s] otherwise (float64 device tensor [b]).  Philox rows are
+    the sequences' indices in this batch."""
+    _on_gpu(target, draft, draft_tokens, temperatures, seeds)
+    if target.dim() != 3 or draft.dim() != 3 or target.stride(2) != 1 or draft.stride(2) != 1:
+        raise ValueError("target [b, K+1, V] and draft [b, K, V] need V contiguous")
+    b, K1, V = target.shape
+    K = K1 - 1
+    if draft.shape != (b, K, V) or draft.dtype != target.dtype:
+        raise ValueError("draft must be [b, K, V] with the target's dtype")
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    if temperatures.shape != (b,) or temperatures.dtype != torch.float64 or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be a contiguous float64 [b] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    dev = target.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           p_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           q_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           argmax=torch.empty(b, K1, dtype=torch.int32, device=dev))
+    need = mixed_workspace_bytes(b, K, V, target.dtype)
+    ws = _workspace(workspace, need, dev)
+    rc = _lib.spec_mixed_accept(
+        target.data_ptr(), draft.data_ptr(), _dtype_code(target), target.stride(0), target.stride(1),
+        draft.stride(0), draft.stride(1), draft_tokens.data_ptr(), b, K, V, temperatures.data_ptr(),
+        seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.p_draft.data_ptr() if out.p_draft is not None else None,
+        out.q_draft.data_ptr() if out.q_draft is not None else None,
+        out.argmax.data_ptr() if out.argmax is not None else None,
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
     _check(rc)
     return out

@@ -6,29 +6,34 @@
 // (row 0 = p_1 from the anchor step, rows 1..K = p_2..p_{K+1} from one verify
 // forward, row K = bonus position; "dspark-mlx 0.1.0" wheel diff,
 // dspark_mlx/adapter.py, "Logit conventions") and, for the sampling rule, a
-// draft block [K, V] with K draft tokens.
+// draft block [K, V] with K draft tokens.  Each sequence follows the greedy
+// rule (temperature 0) or the speculative-sampling rule (temperature T > 0).
 //
-// Kernels (all HBM-bound streaming reductions; no MFMA -- nothing here is a
-// dense contraction):
-//   row_stats_greedy  one wave per 16 KiB row segment: per-lane max and first
-//                     argmax over 16 coalesced 16-byte loads, wave butterfly
-//                     merge (larger value, then lower index).
-//   row_stats_sample  same segment walk over every target and draft row:
-//                     per-lane max, per-lane fp32 sum of exp2((z-m)*log2e/T),
-//                     lane sums merged in double at the wave's max.
-//   scan_greedy       one wave per sequence: fixed-order merge of the segment
-//                     partials, accept-prefix scan, outputs.
-//   scan_sample       one wave per sequence: fixed-order double merge to the
-//                     log-normalisers, gather of z[x_i], Philox uniforms,
-//                     ratio test, outputs, and the draw plan for slot n.
-//   residual_mass     one wave per segment of the rejected row pair:
-//                     sum of max(0, p - q) over the segment.
-//   draw_token        one 256-thread block per sequence: prefix over segment
-//                     masses, re-read of the one segment holding t, block
-//                     prefix sum in double, inverse-CDF search.
+// Kernels (HBM-bound streaming reductions; no MFMA -- nothing here is a dense
+// contraction):
+//   row_pass       one single-wave workgroup per 16 KiB segment of a logit
+//                  row: 16 coalesced nontemporal 16-byte loads per lane,
+//                  then per lane either max + first argmax (greedy rows) or
+//                  max + sum of
+//                  exp2((z - max) * log2(e)/T) (sampling rows), merged across
+//                  the wave by a butterfly (sums in double).
+//   scan           one 1024-thread block per sequence, one wave per row:
+//                  fixed-order merge of the segment partials (double for the
+//                  log-normalisers), then the accept-prefix scan (greedy
+//                  compare, or gather of z[x_i], Philox uniforms and ratio
+//                  test), the outputs and the draw plan for slot n.
+//   residual_mass  one single-wave workgroup per 4 KiB segment of each
+//                  rejected row pair:
+//                  sum of max(0, p - q) over the segment.
+//   draw_token     one 256-thread block per sampling sequence: block scan over
+//                  the segment masses, re-read of the one segment holding t
+//                  into registers, block scan in double, inverse-CDF search.
 //
-// Every merge runs in a fixed order with no floating-point atomics, so two
-// calls on the same bytes give the same bits.
+// Every merge and scan runs in a fixed order with no floating-point atomics,
+// so two calls on the same bytes give the same bits.  Kernel boundaries are
+// the only cross-workgroup synchronisation: a device-scope release fence per
+// workgroup (an L2 write-back on this multi-XCD part) costs far more than a
+// launch.
 
 #include <hip/hip_runtime.h>
 
@@ -44,27 +49,31 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kVecPerLane = 16;                      // 16-byte loads per lane per segment
-constexpr int kSegVec = kWave * kVecPerLane;         // 1024 vectors = 16 KiB per wave
+constexpr int kScanBlock = 1024;                     // scan: one wave per row
+constexpr int kVecPerLane = 16;                      // row pass: 16-byte loads per lane
+constexpr int kSegVec = kWave * kVecPerLane;         // 1024 vectors = 16 KiB per wave segment
+constexpr int kResVecPerLane = 4;                    // residual pass: 4 vectors per lane per row
+constexpr int kResSegVec = kWave * kResVecPerLane;   // 256 vectors = 4 KiB per row per wave
 
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeTarget = 2 };
+enum : int { kRuleInvalid = 0, kRuleGreedy = 1, kRuleSample = 2 };
 
-struct GreedyPartial {
-    float m;        // largest raw logit of the segment
-    int32_t idx;    // its lowest index; -1 when the segment holds NaN or +inf
+// Per-segment statistics of one row.  Greedy rows: m = largest raw logit,
+// idx = its lowest index (-1 if the segment holds NaN or +inf).  Sampling
+// rows: m = largest raw logit (-FLT_MAX if none is finite), S = sum over the
+// segment of exp((z - m) / T).
+struct Partial {
+    float m;
+    int32_t idx;
+    double S;
 };
 
-struct SamplePartial {
-    float m;        // largest raw logit of the segment (-FLT_MAX if none finite)
-    int32_t pad;
-    double S;       // sum over the segment of exp((z - m) / T)
-};
-
-// Draw plan for one sequence, written by scan_sample.
+// Draw plan for one sampling sequence, written by scan.
 struct DrawPlan {
     int32_t mode;       // kModeNone / kModeResidual / kModeTarget
     int32_t slot;       // n: the slot whose token is drawn
     double u2;          // U(seed, s, n, 1)
+    double T;           // the sequence's temperature
     float Mt, Md;       // raw row maxima of target row n and draft row n
     float Lt_hi, Lt_lo; // log2 of the target row's sum at Mt, split hi + lo
     float Ld_hi, Ld_lo; // same for the draft row
@@ -73,7 +82,8 @@ struct DrawPlan {
 
 __host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
 __host__ __device__ constexpr int elem_bytes(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
-__host__ __device__ inline int64_t seg_elems(int dtype) { return (int64_t)kSegVec * elems_per_vec(dtype); }
+__host__ __device__ constexpr int64_t seg_elems(int dtype) { return (int64_t)kSegVec * elems_per_vec(dtype); }
+__host__ __device__ constexpr int64_t rseg_elems(int dtype) { return (int64_t)kResSegVec * elems_per_vec(dtype); }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -109,6 +119,15 @@ __device__ inline float pairwise_sum(const float (&e)[N]) {
     else return (e[0] + e[1]) + (e[2] + e[3]);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of streamed data: nontemporal, so it does not displace
+// anything from the caches.
+__device__ inline uint4 load_stream(const uint4 *p) {
+    u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Vector vi of a row, or -inf padding past the end (element-wise for the one
 // vector that straddles V).
 template <int DT>
@@ -133,21 +152,21 @@ __device__ inline uint4 load_vec_tail(const void *rowp, int64_t vi, int V) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// The 16 vectors a lane owns in segment `seg`: vector seg*1024 + u*64 + lane.
-template <int DT>
-__device__ inline void load_segment(const void *rowp, int seg, int lane, int V, uint4 (&d)[kVecPerLane]) {
-    const int epv = elems_per_vec(DT);
-    const int64_t nfull = (int64_t)V / epv;
-    const int64_t v0 = (int64_t)seg * kSegVec;
+// N vectors of a row for one lane: vector vbase + u*64 + lane, u < N, with
+// -inf past the end of the row.  Vectors wholly inside the row are loaded
+// with streaming 16-byte loads.
+template <int DT, int N>
+__device__ inline void load_vecs(const void *rowp, int64_t vbase, int lane, int V, uint4 (&d)[N]) {
+    const int64_t nfull = (int64_t)V / elems_per_vec(DT);
     const uint4 *vp = (const uint4 *)rowp;
-    if (v0 + kSegVec <= nfull) {
+    if (vbase + (int64_t)N * kWave <= nfull) {
 #pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u) d[u] = vp[v0 + u * kWave + lane];
+        for (int u = 0; u < N; ++u) d[u] = load_stream(vp + vbase + u * kWave + lane);
     } else {
 #pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u) {
-            int64_t vi = v0 + u * kWave + lane;
-            d[u] = vi < nfull ? vp[vi] : load_vec_tail<DT>(rowp, vi, V);
+        for (int u = 0; u < N; ++u) {
+            int64_t vi = vbase + u * kWave + lane;
+            d[u] = vi < nfull ? load_stream(vp + vi) : load_vec_tail<DT>(rowp, vi, V);
         }
     }
 }
@@ -179,11 +198,38 @@ __device__ inline void wave_argmax(float &m, int32_t &idx) {
     }
 }
 
+// Block-wide scan of one double per thread (256 threads): inclusive scan in
+// each wave, then wave offsets added in wave order.  `excl` of thread t is,
+// bit for bit, `incl` of thread t-1 (0 for thread 0), and `total` is `incl`
+// of the last thread, so the intervals [excl, incl) tile [0, total) exactly.
+// Every thread of the block must call it.
+__device__ inline void block_scan(double v, double &excl, double &incl, double &total, double *sw) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    double x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) sw[w] = x;
+    __syncthreads();
+    double woff = 0.0;
+    for (int k = 0; k < w; ++k) woff += sw[k];
+    double tot = 0.0;
+    for (int k = 0; k < kWavesPerBlock; ++k) tot += sw[k];
+    __syncthreads();
+    incl = woff + x;
+    const double prev = __shfl_up(incl, 1, kWave);
+    excl = lane == 0 ? woff : prev;
+    total = tot;
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies by the round multipliers with the high halves xored
 // into the other counter words and the round key; the key advances by the two
-// Weyl increments between rounds.
+// Weyl increments between rounds.  U = top 24 bits of output word 0 * 2^-24.
 
 __device__ inline double philox_uniform(uint64_t seed, uint32_t row, uint32_t pos, uint32_t tag) {
     uint32_t x0 = pos, x1 = row, x2 = tag, x3 = 0u;
@@ -206,7 +252,24 @@ __device__ inline double philox_uniform(uint64_t seed, uint32_t row, uint32_t po
 }
 
 // ---------------------------------------------------------------------------
-// Row addressing.  `row` enumerates (sequence, row-in-block) pairs.
+// Rules and scales.
+
+// Temperature 0 is the greedy rule, a finite positive temperature the
+// sampling rule; anything else makes the sequence invalid.
+__device__ inline int rule_of(double T) {
+    if (T == 0.0) return kRuleGreedy;
+    if (T > 0.0 && T < INFINITY) return kRuleSample;
+    return kRuleInvalid;
+}
+
+// log2(e)/T as c_hi + c_lo: c_hi rounded down, c_lo >= FLT_MIN, so both
+// products of a -inf logit difference stay -inf (never -inf + inf = NaN).
+__device__ inline void split_scale(double T, float &c_hi, float &c_lo, double &c64) {
+    c64 = 1.4426950408889634 / T;
+    c_hi = __double2float_rd(c64);
+    const float lo = (float)(c64 - (double)c_hi);
+    c_lo = lo < FLT_MIN ? FLT_MIN : lo;
+}
 
 template <int DT>
 __device__ inline const void *row_ptr(const void *base, int64_t bstride, int64_t rstride, int s, int i) {
@@ -214,269 +277,326 @@ __device__ inline const void *row_ptr(const void *base, int64_t bstride, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Greedy row pass.
+// Per-call parameters shared by every device role.
+
+struct Ctx {
+    const void *target, *draft;
+    int64_t tbs, trs, dbs, drs;        // element strides
+    int K, V, nseg, nres, rps;         // rps: partial rows per sequence (K+1 or 2K+1)
+    const double *temps;               // per-sequence temperatures, or NULL
+    double T_uniform;                  // the call's temperature when temps is NULL
+    const int32_t *x;                  // draft tokens [b, K]
+    const uint64_t *seeds;             // [b]
+    int32_t *n_out, *tok;              // [b], [b, K+1]
+    float *p_out, *q_out;              // [b, K] or NULL
+    int32_t *am;                       // [b, K+1] or NULL
+    Partial *part;                     // [b, rps, nseg]
+    DrawPlan *plan;                    // [b] or NULL (greedy-only calls)
+    double *rmass;                     // [b, nres] or NULL
+};
+
+__device__ inline double seq_temperature(const Ctx &c, int s) { return c.temps ? c.temps[s] : c.T_uniform; }
+
+// ---------------------------------------------------------------------------
+// Row pass, one wave: segment `seg` of row i of sequence s.  Greedy rows keep
+// max + first argmax; sampling rows keep max + sum of exp2((z - max) c).
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void row_stats_greedy(
-    const void *__restrict__ target, int64_t bs, int64_t rs, int K1, int V, int nseg,
-    int seg_blocks, GreedyPartial *__restrict__ part) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x / seg_blocks;
-    const int seg = (blockIdx.x - row * seg_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (seg >= nseg) return;
-    const int s = row / K1, i = row - s * K1;
-    const void *rowp = row_ptr<DT>(target, bs, rs, s, i);
-
-    float mx = -INFINITY;
-    int32_t ix = INT_MAX;
-    bool bad = false;
-    if constexpr (VEC) {
-        uint4 d[kVecPerLane];
-        load_segment<DT>(rowp, seg, lane, V, d);
-        const int epv = elems_per_vec(DT);
+__device__ inline void row_wave(const Ctx &c, int s, int i, int seg, int lane, int rule, double T) {
+    const int K = c.K, V = c.V;
+    const void *rowp = i <= K ? row_ptr<DT>(c.target, c.tbs, c.trs, s, i)
+                              : row_ptr<DT>(c.draft, c.dbs, c.drs, s, i - K - 1);
+    Partial out;
+    if (rule == kRuleGreedy) {
+        float mx = -INFINITY;
+        int32_t ix = INT_MAX;
+        bool bad = false;
+        if constexpr (VEC) {
+            uint4 d[kVecPerLane];
+            load_vecs<DT, kVecPerLane>(rowp, (int64_t)seg * kSegVec, lane, V, d);
 #pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u) {
-            const int32_t e0 = (int32_t)(((int64_t)seg * kSegVec + u * kWave + lane) * epv);
+            for (int u = 0; u < kVecPerLane; ++u) {
+                const int32_t e0 = (int32_t)(((int64_t)seg * kSegVec + u * kWave + lane) * elems_per_vec(DT));
 #pragma unroll
-            for (int k = 0; k < elems_per_vec(DT); ++k) {
-                float f = vec_elem<DT>(d[u], k);
+                for (int k = 0; k < elems_per_vec(DT); ++k) {
+                    const float f = vec_elem<DT>(d[u], k);
+                    bad |= !(f < INFINITY);
+                    if (f > mx) {
+                        mx = f;
+                        ix = e0 + k;
+                    }
+                }
+            }
+        } else {
+            const int64_t e_begin = (int64_t)seg * seg_elems(DT);
+            const int64_t e_end = min((int64_t)V, e_begin + seg_elems(DT));
+            for (int64_t e = e_begin + lane; e < e_end; e += kWave) {
+                const float f = elem_at<DT>(rowp, e);
                 bad |= !(f < INFINITY);
                 if (f > mx) {
                     mx = f;
-                    ix = e0 + k;
+                    ix = (int32_t)e;
                 }
             }
         }
-    } else {
-        const int64_t e_begin = (int64_t)seg * seg_elems(DT);
-        const int64_t e_end = min((int64_t)V, e_begin + seg_elems(DT));
-        for (int64_t e = e_begin + lane; e < e_end; e += kWave) {
-            float f = elem_at<DT>(rowp, e);
-            bad |= !(f < INFINITY);
-            if (f > mx) {
-                mx = f;
-                ix = (int32_t)e;
-            }
-        }
-    }
-    wave_argmax(mx, ix);
-    const bool any_bad = __ballot(bad) != 0ull;
-    if (lane == 0) {
-        GreedyPartial p;
-        p.m = mx;
-        p.idx = any_bad ? -1 : ix;
-        part[(int64_t)row * nseg + seg] = p;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Sampling row pass.  c_hi + c_lo = log2(e) / T with c_hi rounded down and
-// c_lo >= FLT_MIN, so that z = -inf gives exp2(-inf) = 0 and never NaN.
-
-template <int DT>
-__device__ inline float scaled_exp2(float dz, float c_hi, float c_lo) {
-    return __builtin_amdgcn_exp2f(fmaf(dz, c_hi, dz * c_lo));
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void row_stats_sample(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    int64_t tbs, int64_t trs, int64_t dbs, int64_t drs, int K, int V, int nseg,
-    int seg_blocks, float c_hi, float c_lo, double c64, SamplePartial *__restrict__ part) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x / seg_blocks;
-    const int seg = (blockIdx.x - row * seg_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (seg >= nseg) return;
-    const int R = 2 * K + 1;
-    const int s = row / R, i = row - s * R;
-    const void *rowp = i <= K ? row_ptr<DT>(target, tbs, trs, s, i)
-                              : row_ptr<DT>(draft, dbs, drs, s, i - K - 1);
-
-    // Per lane: max, then the sum of exp2 at that max -- pairwise in fp32
-    // inside each 16-byte vector, in double across vectors.
-    float ml = -FLT_MAX;
-    double sl = 0.0;
-    if constexpr (VEC) {
-        uint4 d[kVecPerLane];
-        load_segment<DT>(rowp, seg, lane, V, d);
-#pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u)
-#pragma unroll
-            for (int k = 0; k < elems_per_vec(DT); ++k) ml = fmaxf(ml, vec_elem<DT>(d[u], k));
-#pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u) {
-            float e[elems_per_vec(DT)];
-#pragma unroll
-            for (int k = 0; k < elems_per_vec(DT); ++k)
-                e[k] = scaled_exp2<DT>(vec_elem<DT>(d[u], k) - ml, c_hi, c_lo);
-            sl += (double)pairwise_sum<elems_per_vec(DT)>(e);
-        }
-    } else {
-        const int64_t e_begin = (int64_t)seg * seg_elems(DT);
-        const int64_t e_end = min((int64_t)V, e_begin + seg_elems(DT));
-        for (int64_t e = e_begin + lane; e < e_end; e += kWave) ml = fmaxf(ml, elem_at<DT>(rowp, e));
-        for (int64_t e = e_begin + lane; e < e_end; e += kWave)
-            sl += (double)scaled_exp2<DT>(elem_at<DT>(rowp, e) - ml, c_hi, c_lo);
-    }
-    const float mw = wave_max(ml);
-    const double contrib = sl * exp2(((double)ml - (double)mw) * c64);
-    const double Sw = wave_sum(contrib);
-    if (lane == 0) {
-        SamplePartial p;
-        p.m = mw;
-        p.pad = 0;
-        p.S = Sw;
-        part[(int64_t)row * nseg + seg] = p;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Greedy accept-prefix scan: one wave per sequence.
-
-__global__ __launch_bounds__(kWave) void scan_greedy(
-    const GreedyPartial *__restrict__ part, int nseg, int K, int V,
-    const int32_t *__restrict__ draft_tokens, int32_t *__restrict__ n_out,
-    int32_t *__restrict__ tokens, int32_t *__restrict__ argmax_out) {
-    const int s = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int K1 = K + 1;
-    __shared__ int32_t sA[SPEC_MAX_K + 1];
-    __shared__ int32_t sBad;
-    if (lane == 0) sBad = 0;
-    __syncthreads();
-    for (int i = 0; i < K1; ++i) {
-        const GreedyPartial *pr = part + ((int64_t)s * K1 + i) * nseg;
-        float m = -INFINITY;
-        int32_t idx = INT_MAX;
-        bool bad = false;
-        for (int j = lane; j < nseg; j += kWave) {   // ascending segments: ties keep the lower index
-            GreedyPartial p = pr[j];
-            if (p.idx < 0) bad = true;
-            else if (p.m > m) {
-                m = p.m;
-                idx = p.idx;
-            }
-        }
-        wave_argmax(m, idx);
+        wave_argmax(mx, ix);
         const bool any_bad = __ballot(bad) != 0ull;
-        if (lane == 0) {
-            sA[i] = idx;
-            if (any_bad || !(m > -INFINITY)) sBad = 1;
+        out.m = mx;
+        out.idx = any_bad ? -1 : ix;
+        out.S = 0.0;
+    } else {
+        float c_hi, c_lo;
+        double c64;
+        split_scale(T, c_hi, c_lo, c64);
+        // Per lane: max, then the sum of exp2 at that max -- pairwise in fp32
+        // inside each 16-byte vector, in double across vectors.
+        float ml = -FLT_MAX;
+        double sl = 0.0;
+        if constexpr (VEC) {
+            uint4 d[kVecPerLane];
+            load_vecs<DT, kVecPerLane>(rowp, (int64_t)seg * kSegVec, lane, V, d);
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u)
+#pragma unroll
+                for (int k = 0; k < elems_per_vec(DT); ++k) ml = fmaxf(ml, vec_elem<DT>(d[u], k));
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u) {
+                float e[elems_per_vec(DT)];
+#pragma unroll
+                for (int k = 0; k < elems_per_vec(DT); ++k) {
+                    const float dz = vec_elem<DT>(d[u], k) - ml;
+                    e[k] = __builtin_amdgcn_exp2f(fmaf(dz, c_hi, dz * c_lo));
+                }
+                sl += (double)pairwise_sum<elems_per_vec(DT)>(e);
+            }
+        } else {
+            const int64_t e_begin = (int64_t)seg * seg_elems(DT);
+            const int64_t e_end = min((int64_t)V, e_begin + seg_elems(DT));
+            for (int64_t e = e_begin + lane; e < e_end; e += kWave) ml = fmaxf(ml, elem_at<DT>(rowp, e));
+            for (int64_t e = e_begin + lane; e < e_end; e += kWave) {
+                const float dz = elem_at<DT>(rowp, e) - ml;
+                sl += (double)__builtin_amdgcn_exp2f(fmaf(dz, c_hi, dz * c_lo));
+            }
         }
+        const float mw = wave_max(ml);
+        out.m = mw;
+        out.idx = 0;
+        out.S = wave_sum(sl * exp2(((double)ml - (double)mw) * c64));
     }
-    __syncthreads();
-    bool tok_bad = false;
-    if (lane < K) {
-        int32_t x = draft_tokens[(int64_t)s * K + lane];
-        tok_bad = x < 0 || x >= V;
-    }
-    const bool invalid = sBad || (__ballot(tok_bad) != 0ull);
-    int32_t *tok = tokens + (int64_t)s * K1;
-    if (invalid) {
-        if (lane < K1) {
-            tok[lane] = -1;
-            if (argmax_out) argmax_out[(int64_t)s * K1 + lane] = -1;
-        }
-        if (lane == 0) n_out[s] = -1;
-        return;
-    }
-    bool mismatch = false;
-    if (lane < K) mismatch = draft_tokens[(int64_t)s * K + lane] != sA[lane];
-    const unsigned long long mm = __ballot(mismatch);
-    const int n = mm ? (int)__ffsll((long long)mm) - 1 : K;
-    if (lane < K1) {
-        int32_t t = lane < n ? draft_tokens[(int64_t)s * K + lane] : lane == n ? sA[n] : -1;
-        tok[lane] = t;
-        if (argmax_out) argmax_out[(int64_t)s * K1 + lane] = sA[lane];
-    }
-    if (lane == 0) n_out[s] = n;
+    if (lane == 0) c.part[((int64_t)s * c.rps + i) * c.nseg + seg] = out;
 }
 
 // ---------------------------------------------------------------------------
-// Sampling accept scan: one wave per sequence.
+// Accept scan of one sequence by one block of NW waves.  Wave w merges rows
+// w, w + NW, ... (each wave's first kPre row loads issued together, before
+// the temperature decides the rule); wave 0 then runs the scan.
 
-template <int DT>
-__global__ __launch_bounds__(kWave) void scan_sample(
-    const SamplePartial *__restrict__ part, int nseg, int K, int V, double T, double c64,
-    const void *__restrict__ target, const void *__restrict__ draft,
-    int64_t tbs, int64_t trs, int64_t dbs, int64_t drs,
-    const int32_t *__restrict__ draft_tokens, const uint64_t *__restrict__ seeds,
-    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens,
-    float *__restrict__ p_out, float *__restrict__ q_out, DrawPlan *__restrict__ plan) {
-    const int s = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int R = 2 * K + 1;
+constexpr int kPre = 4;
+
+template <int DT, int NW>
+__device__ inline void scan_seq(const Ctx &c, int s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int K = c.K, V = c.V, nseg = c.nseg, rps = c.rps;
+    const int K1 = K + 1;
     __shared__ float sM[2 * SPEC_MAX_K + 1];
     __shared__ double sS[2 * SPEC_MAX_K + 1];
+    __shared__ int32_t sA[SPEC_MAX_K + 1];
+    __shared__ int32_t sBad;
 
-    bool row_bad = false;
-    for (int r = 0; r < R; ++r) {
-        const SamplePartial *pr = part + ((int64_t)s * R + r) * nseg;
+    Partial pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        pre[k].m = -FLT_MAX;
+        pre[k].idx = INT_MAX;
+        pre[k].S = 0.0;
+        const int r = wave + k * NW;
+        if (r < rps && lane < nseg) pre[k] = c.part[((int64_t)s * rps + r) * nseg + lane];
+    }
+    const double T = seq_temperature(c, s);
+    const int rule = rule_of(T);
+    int32_t *tok = c.tok + (int64_t)s * K1;
+
+    if (rule == kRuleInvalid) {
+        if (wave != 0) return;
+        if (lane < K1) {
+            tok[lane] = -1;
+            if (c.am) c.am[(int64_t)s * K1 + lane] = -1;
+        }
+        if (lane < K) {
+            if (c.p_out) c.p_out[(int64_t)s * K + lane] = NAN;
+            if (c.q_out) c.q_out[(int64_t)s * K + lane] = NAN;
+        }
+        if (lane == 0) {
+            c.n_out[s] = -1;
+            if (c.plan) {
+                DrawPlan pl = {};
+                pl.mode = kModeNone;
+                c.plan[s] = pl;
+            }
+        }
+        return;
+    }
+
+    if (threadIdx.x == 0) sBad = 0;
+    __syncthreads();
+
+    // Wave 0 reads the draft tokens (and, sampling, gathers z[x_i]) while the
+    // other waves merge.
+    int32_t x = 0;
+    bool tok_bad = false;
+    float zt = 0.0f, zd = 0.0f;
+    if (wave == 0 && lane < K) {
+        x = c.x[(int64_t)s * K + lane];
+        tok_bad = x < 0 || x >= V;
+        if (rule == kRuleSample && !tok_bad) {
+            zt = elem_at<DT>(row_ptr<DT>(c.target, c.tbs, c.trs, s, lane), x);
+            zd = elem_at<DT>(row_ptr<DT>(c.draft, c.dbs, c.drs, s, lane), x);
+        }
+    }
+
+    if (rule == kRuleGreedy) {
+        // Row i: (max, lowest argmax) over ascending segments, the first
+        // segment of this lane from `first` when it was preloaded.
+        auto merge_row = [&](int i, const Partial *first) {
+            const Partial *pr = c.part + ((int64_t)s * rps + i) * nseg;
+            float m = -INFINITY;
+            int32_t idx = INT_MAX;
+            bool bad = false;
+            auto take = [&](const Partial &p) {
+                if (p.idx < 0) bad = true;
+                else if (p.m > m) {
+                    m = p.m;
+                    idx = p.idx;
+                }
+            };
+            int j = lane;
+            if (first) {
+                if (j < nseg) take(*first);
+                j += kWave;
+            }
+            for (; j < nseg; j += kWave) take(pr[j]);
+            wave_argmax(m, idx);
+            const bool any_bad = __ballot(bad) != 0ull;
+            if (lane == 0) {
+                sA[i] = idx;
+                if (any_bad || !(m > -INFINITY)) sBad = 1;
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < kPre; ++k)
+            if (wave + k * NW < K1) merge_row(wave + k * NW, &pre[k]);
+        for (int i = wave + kPre * NW; i < K1; i += NW) merge_row(i, nullptr);
+        __syncthreads();
+        if (wave != 0) return;
+        const bool invalid = sBad || (__ballot(tok_bad) != 0ull);
+        if (lane < K) {
+            if (c.p_out) c.p_out[(int64_t)s * K + lane] = NAN;
+            if (c.q_out) c.q_out[(int64_t)s * K + lane] = NAN;
+        }
+        if (lane == 0 && c.plan) {
+            DrawPlan pl = {};
+            pl.mode = kModeNone;
+            c.plan[s] = pl;
+        }
+        if (invalid) {
+            if (lane < K1) {
+                tok[lane] = -1;
+                if (c.am) c.am[(int64_t)s * K1 + lane] = -1;
+            }
+            if (lane == 0) c.n_out[s] = -1;
+            return;
+        }
+        const bool mismatch = lane < K && x != sA[lane];
+        const unsigned long long mm = __ballot(mismatch);
+        const int n = mm ? (int)__ffsll((long long)mm) - 1 : K;
+        if (lane < K1) {
+            tok[lane] = lane < n ? x : lane == n ? sA[n] : -1;
+            if (c.am) c.am[(int64_t)s * K1 + lane] = sA[lane];
+        }
+        if (lane == 0) c.n_out[s] = n;
+        return;
+    }
+
+    // Sampling: log-normalisers of the 2K+1 rows.
+    const int R = 2 * K + 1;
+    const double c64 = 1.4426950408889634 / T;
+    // Row r: M = max of the segment maxima, S = sum of the segment sums
+    // rescaled to M (double), the first segment of this lane from `first`.
+    auto merge_row = [&](int r, const Partial *first) {
+        const Partial *pr = c.part + ((int64_t)s * rps + r) * nseg;
         float m = -FLT_MAX;
-        for (int j = lane; j < nseg; j += kWave) m = fmaxf(m, pr[j].m);
+        int j = lane;
+        if (first) {
+            if (j < nseg) m = fmaxf(m, first->m);
+            j += kWave;
+        }
+        for (; j < nseg; j += kWave) m = fmaxf(m, pr[j].m);
         const float M = wave_max(m);
         double acc = 0.0;
-        for (int j = lane; j < nseg; j += kWave) {
-            SamplePartial p = pr[j];
+        j = lane;
+        if (first) {
+            if (j < nseg) acc += first->S * exp2(((double)first->m - (double)M) * c64);
+            j += kWave;
+        }
+        for (; j < nseg; j += kWave) {
+            const Partial p = pr[j];
             acc += p.S * exp2(((double)p.m - (double)M) * c64);
         }
         const double S = wave_sum(acc);
         if (lane == 0) {
             sM[r] = M;
             sS[r] = S;
+            if (!(S > 0.0) || !(S < INFINITY)) sBad = 1;   // NaN/+inf seen, or no finite entry
         }
-        if (!(S > 0.0) || !(S < INFINITY)) row_bad = true;   // NaN/+inf seen, or no finite entry
-    }
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (wave + k * NW < R) merge_row(wave + k * NW, &pre[k]);
+    for (int r = wave + kPre * NW; r < R; r += NW) merge_row(r, nullptr);
     __syncthreads();
+    if (wave != 0) return;
 
-    const uint64_t seed = seeds[s];
-    int32_t x = 0;
-    bool tok_bad = false;
-    if (lane < K) {
-        x = draft_tokens[(int64_t)s * K + lane];
-        tok_bad = x < 0 || x >= V;
-    }
-    const bool invalid = row_bad || (__ballot(tok_bad) != 0ull);
-    int32_t *tok = tokens + (int64_t)s * (K + 1);
+    if (c.am && lane < K1) c.am[(int64_t)s * K1 + lane] = -1;
+    const bool invalid = sBad || (__ballot(tok_bad) != 0ull);
     if (invalid) {
-        if (lane <= K) tok[lane] = -1;
+        if (lane < K1) tok[lane] = -1;
         if (lane < K) {
-            if (p_out) p_out[(int64_t)s * K + lane] = NAN;
-            if (q_out) q_out[(int64_t)s * K + lane] = NAN;
+            if (c.p_out) c.p_out[(int64_t)s * K + lane] = NAN;
+            if (c.q_out) c.q_out[(int64_t)s * K + lane] = NAN;
         }
         if (lane == 0) {
-            n_out[s] = -1;
             DrawPlan pl = {};
             pl.mode = kModeNone;
-            plan[s] = pl;
+            c.plan[s] = pl;
+            c.n_out[s] = -1;
         }
         return;
     }
-
+    const uint64_t seed = c.seeds[s];
     bool reject = false;
     if (lane < K) {
-        const float zt = elem_at<DT>(row_ptr<DT>(target, tbs, trs, s, lane), x);
-        const float zd = elem_at<DT>(row_ptr<DT>(draft, dbs, drs, s, lane), x);
         const double lp = ((double)zt - (double)sM[lane]) / T - log(sS[lane]);
-        const double lq = ((double)zd - (double)sM[K + 1 + lane]) / T - log(sS[K + 1 + lane]);
+        const double lq = ((double)zd - (double)sM[K1 + lane]) / T - log(sS[K1 + lane]);
         double r;
         if (zt == -INFINITY) r = 0.0;                 // p(x) = 0: never accepted
         else if (zd == -INFINITY) r = INFINITY;       // q(x) = 0 < p(x): always accepted
         else r = exp(lp - lq);
         const double u = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 0u);
         reject = !(u < r);                            // u < 1, so u < r == u < min(1, r)
-        if (p_out) p_out[(int64_t)s * K + lane] = (float)exp(lp);
-        if (q_out) q_out[(int64_t)s * K + lane] = (float)exp(lq);
+        if (c.p_out) c.p_out[(int64_t)s * K + lane] = (float)exp(lp);
+        if (c.q_out) c.q_out[(int64_t)s * K + lane] = (float)exp(lq);
     }
     const unsigned long long rj = __ballot(reject);
     const int n = rj ? (int)__ffsll((long long)rj) - 1 : K;
-    if (lane <= K) tok[lane] = lane < n ? x : -1;    // slot n is filled by draw_token
+    if (lane < K1) tok[lane] = lane < n ? x : -1;     // slot n is filled by the draw
     if (lane == 0) {
-        n_out[s] = n;
+        c.n_out[s] = n;
         DrawPlan pl;
         pl.mode = n < K ? kModeResidual : kModeTarget;
         pl.slot = n;
         pl.u2 = philox_uniform(seed, (uint32_t)s, (uint32_t)n, 1u);
+        pl.T = T;
         const double St = sS[n];
         const double Lt = log2(St);
         pl.Mt = sM[n];
@@ -484,8 +604,8 @@ __global__ __launch_bounds__(kWave) void scan_sample(
         pl.Lt_hi = (float)Lt;
         pl.Lt_lo = (float)(Lt - (double)pl.Lt_hi);
         if (n < K) {
-            const double Ld = log2(sS[K + 1 + n]);
-            pl.Md = sM[K + 1 + n];
+            const double Ld = log2(sS[K1 + n]);
+            pl.Md = sM[K1 + n];
             pl.Ld_hi = (float)Ld;
             pl.Ld_lo = (float)(Ld - (double)pl.Ld_hi);
         } else {
@@ -493,49 +613,48 @@ __global__ __launch_bounds__(kWave) void scan_sample(
             pl.Ld_hi = 0.0f;
             pl.Ld_lo = 0.0f;
         }
-        plan[s] = pl;
+        c.plan[s] = pl;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Draw weights.  p(v) = exp2((z - M) * log2(e)/T - log2 S), evaluated as
 // fma(dz, c_hi, -L_hi) + fma(dz, c_lo, -L_lo) so the large terms cancel inside
-// one rounding.  residual_mass and draw_token call the same function on the
-// same constants, so a weight has the same bits in both.
+// one rounding.  A -inf logit gives -inf in both products (c_hi, c_lo > 0),
+// hence weight 0.  The residual pass and the draw call the same function on
+// the same constants, so a weight has the same bits in both.
 
 __device__ inline float target_weight(float zt, const DrawPlan &pl, float c_hi, float c_lo) {
-    const float dz = fmaxf(zt - pl.Mt, -3.0e38f);
+    const float dz = zt - pl.Mt;
     return __builtin_amdgcn_exp2f(fmaf(dz, c_hi, -pl.Lt_hi) + fmaf(dz, c_lo, -pl.Lt_lo));
 }
 
 __device__ inline float residual_weight(float zt, float zd, const DrawPlan &pl, float c_hi, float c_lo) {
-    const float dzd = fmaxf(zd - pl.Md, -3.0e38f);
+    const float dzd = zd - pl.Md;
     const float q = __builtin_amdgcn_exp2f(fmaf(dzd, c_hi, -pl.Ld_hi) + fmaf(dzd, c_lo, -pl.Ld_lo));
     const float w = target_weight(zt, pl, c_hi, c_lo) - q;
     return w > 0.0f ? w : 0.0f;
 }
 
-// Segment masses of max(0, p_n - q_n) for sequences that rejected a slot.
+// Residual mass of segment `seg` of sequence s's rejected row pair, one wave.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void residual_mass(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    int64_t tbs, int64_t trs, int64_t dbs, int64_t drs, int V, int nseg, int seg_blocks,
-    float c_hi, float c_lo, const DrawPlan *__restrict__ plan, double *__restrict__ rmass) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = blockIdx.x / seg_blocks;
-    const int seg = (blockIdx.x - s * seg_blocks) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (seg >= nseg) return;
-    const DrawPlan pl = plan[s];
+__device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
+    const DrawPlan pl = c.plan[s];
     if (pl.mode != kModeResidual) return;
-    const void *tp = row_ptr<DT>(target, tbs, trs, s, pl.slot);
-    const void *dp = row_ptr<DT>(draft, dbs, drs, s, pl.slot);
+    const int V = c.V;
+    float c_hi, c_lo;
+    double c64;
+    split_scale(pl.T, c_hi, c_lo, c64);
+    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
+    const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
     double acc = 0.0;
     if constexpr (VEC) {
-        uint4 a[kVecPerLane], b[kVecPerLane];
-        load_segment<DT>(tp, seg, lane, V, a);
-        load_segment<DT>(dp, seg, lane, V, b);
+        uint4 a[kResVecPerLane], b[kResVecPerLane];
+        const int64_t vbase = (int64_t)seg * kResSegVec;
+        load_vecs<DT, kResVecPerLane>(tp, vbase, lane, V, a);
+        load_vecs<DT, kResVecPerLane>(dp, vbase, lane, V, b);
 #pragma unroll
-        for (int u = 0; u < kVecPerLane; ++u) {
+        for (int u = 0; u < kResVecPerLane; ++u) {
             float w[elems_per_vec(DT)];
 #pragma unroll
             for (int k = 0; k < elems_per_vec(DT); ++k)
@@ -543,149 +662,225 @@ __global__ __launch_bounds__(kBlock) void residual_mass(
             acc += (double)pairwise_sum<elems_per_vec(DT)>(w);
         }
     } else {
-        const int64_t e_begin = (int64_t)seg * seg_elems(DT);
-        const int64_t e_end = min((int64_t)V, e_begin + seg_elems(DT));
+        const int64_t e_begin = (int64_t)seg * rseg_elems(DT);
+        const int64_t e_end = min((int64_t)V, e_begin + rseg_elems(DT));
         for (int64_t e = e_begin + lane; e < e_end; e += kWave)
             acc += (double)residual_weight(elem_at<DT>(tp, e), elem_at<DT>(dp, e), pl, c_hi, c_lo);
     }
     const double Sw = wave_sum(acc);
-    if (lane == 0) rmass[(int64_t)s * nseg + seg] = Sw;
+    if (lane == 0) c.rmass[(int64_t)s * c.nres + seg] = Sw;
 }
 
-// Block-wide exclusive prefix over one double per thread, in thread order
-// (thread 0 adds them up sequentially: the order never changes).
-__device__ inline double block_exclusive_prefix(double v, double *sbuf, double &total) {
-    sbuf[threadIdx.x] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double run = 0.0;
-        for (int t = 0; t < kBlock; ++t) {
-            double x = sbuf[t];
-            sbuf[t] = run;
-            run += x;
+// Inverse-CDF search inside one segment [e_seg0, e_seg0 + 256*E) of the
+// drawn row: thread t holds elements e_seg0 + t*E .. + E - 1 in registers.
+// Writes the drawn index to *sY (or the segment's last positive weight to
+// *sLastPos when tl sits at or past the segment's recomputed total).
+template <int DT, bool VEC, int E, bool RESID>
+__device__ inline void search_segment(const void *tp, const void *dp, int64_t e_seg0, int V, const DrawPlan &pl,
+                                      float c_hi, float c_lo, double tl, double *sw, int32_t *sY,
+                                      int32_t *sLastPos) {
+    constexpr int EPV = elems_per_vec(DT);
+    const int64_t e0 = e_seg0 + (int64_t)threadIdx.x * E;
+    float w[E];
+    if (VEC && E % EPV == 0 && e0 + E <= V) {
+        constexpr int NV = E / EPV;
+        uint4 a[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) a[u] = ((const uint4 *)tp)[e0 / EPV + u];
+        if constexpr (RESID) {
+            uint4 b[NV];
+#pragma unroll
+            for (int u = 0; u < NV; ++u) b[u] = ((const uint4 *)dp)[e0 / EPV + u];
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+#pragma unroll
+                for (int k = 0; k < EPV; ++k)
+                    w[u * EPV + k] = residual_weight(vec_elem<DT>(a[u], k), vec_elem<DT>(b[u], k), pl, c_hi, c_lo);
+        } else {
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) w[u * EPV + k] = target_weight(vec_elem<DT>(a[u], k), pl, c_hi, c_lo);
         }
-        sbuf[kBlock] = run;
+    } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int64_t e = e0 + k;
+            float wk = 0.0f;
+            if (e < V) {
+                if constexpr (RESID) wk = residual_weight(elem_at<DT>(tp, e), elem_at<DT>(dp, e), pl, c_hi, c_lo);
+                else wk = target_weight(elem_at<DT>(tp, e), pl, c_hi, c_lo);
+            }
+            w[k] = wk;
+        }
     }
-    __syncthreads();
-    const double pre = sbuf[threadIdx.x];
-    total = sbuf[kBlock];
-    __syncthreads();
-    return pre;
+    double tsum = 0.0;
+    int32_t lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        tsum += (double)w[k];
+        if (w[k] > 0.0f) lastpos = (int32_t)(e0 + k);
+    }
+    double wex, win, segtotal;
+    block_scan(tsum, wex, win, segtotal, sw);
+    if (!(tl < segtotal)) {
+        if (lastpos >= 0) atomicMax(sLastPos, lastpos);
+    } else if (wex <= tl && tl < win) {
+        double run = wex;
+        int32_t y = lastpos;                           // rounding fallback
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            run += (double)w[k];
+            if (run > tl) {
+                y = (int32_t)(e0 + k);
+                break;
+            }
+        }
+        *sY = y;
+    }
 }
 
-// Draw the token of slot n: inverse CDF over ascending vocabulary index of
-// the residual (mode residual) or of p_n (mode target: the bonus, or a
+// Draw the token of slot n of sequence s (one 256-thread block): inverse CDF
+// over ascending vocabulary index of the residual (mode residual, residual
+// segments) or of p_n (mode target, row-pass segments: the bonus, or a
 // rejected slot whose residual mass is zero).
-template <int DT>
-__global__ __launch_bounds__(kBlock) void draw_token(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    int64_t tbs, int64_t trs, int64_t dbs, int64_t drs, int K, int V, int nseg,
-    float c_hi, float c_lo, double c64, const SamplePartial *__restrict__ spart,
-    const double *__restrict__ rmass, const DrawPlan *__restrict__ plan,
-    int32_t *__restrict__ tokens) {
-    const int s = blockIdx.x;
+template <int DT, bool VEC>
+__device__ inline void draw_seq(const Ctx &c, int s) {
     const int t = threadIdx.x;
-    __shared__ double sbuf[kBlock + 1];
+    const int K = c.K, V = c.V, nseg = c.nseg, nres = c.nres;
+    __shared__ double sw[kWavesPerBlock];
     __shared__ int32_t sSeg;
     __shared__ double sOff;
     __shared__ int32_t sY;
+    __shared__ int32_t sLastPos;
 
-    const DrawPlan pl = plan[s];
+    // The residual masses of this thread's range are loaded together with the
+    // plan (their address does not depend on it); unused when the plan says
+    // otherwise.
+    const double *rm = c.rmass + (int64_t)s * nres;
+    const int rper = (nres + kBlock - 1) / kBlock;
+    const int r0 = min(nres, t * rper);
+    const double rm_first = r0 < min(nres, r0 + rper) ? rm[r0] : 0.0;
+    const DrawPlan pl = c.plan[s];
     if (pl.mode == kModeNone) return;
-    int mode = pl.mode;
-    const int R = 2 * K + 1;
-    const SamplePartial *tpart = spart + ((int64_t)s * R + pl.slot) * nseg;
-    const double *rm = rmass + (int64_t)s * nseg;
+    float c_hi, c_lo;
+    double c64;
+    split_scale(pl.T, c_hi, c_lo, c64);
+    const Partial *tpart = c.part + ((int64_t)s * c.rps + pl.slot) * nseg;
+    bool resid = pl.mode == kModeResidual;
 
-    // Segment masses, summed per thread over a contiguous range of segments
-    // (sequentially from zero), then an exclusive prefix over threads.
-    auto seg_mass = [&](int j, int md) -> double {
-        return md == kModeResidual ? rm[j]
-                                   : tpart[j].S * exp2(((double)tpart[j].m - (double)pl.Mt) * c64) / pl.St;
+    // (a) segment masses: thread t sums a contiguous range of segments.
+    auto seg_mass = [&](int j) -> double {
+        return resid ? rm[j] : tpart[j].S * exp2(((double)tpart[j].m - (double)pl.Mt) * c64) / pl.St;
     };
-    const int per = (nseg + kBlock - 1) / kBlock;
-    const int j0 = min(nseg, t * per), j1 = min(nseg, j0 + per);
-    double local = 0.0, total = 0.0, pre = 0.0;
-    for (int pass = 0; pass < 2; ++pass) {
+    int nsg = resid ? nres : nseg;
+    int per = (nsg + kBlock - 1) / kBlock;
+    int j0 = min(nsg, t * per), j1 = min(nsg, j0 + per);
+    double local = 0.0, excl, incl, total;
+    for (int j = j0; j < j1; ++j) local += (resid && j == r0) ? rm_first : seg_mass(j);
+    block_scan(local, excl, incl, total, sw);
+    if (resid && !(total > 0.0)) {                     // zero residual mass: draw from p_n
+        resid = false;
+        nsg = nseg;
+        per = (nsg + kBlock - 1) / kBlock;
+        j0 = min(nsg, t * per);
+        j1 = min(nsg, j0 + per);
         local = 0.0;
-        for (int j = j0; j < j1; ++j) local += seg_mass(j, mode);
-        pre = block_exclusive_prefix(local, sbuf, total);
-        if (mode == kModeResidual && !(total > 0.0)) {
-            mode = kModeTarget;            // zero residual mass: draw from p_n
-            continue;
-        }
-        break;
+        for (int j = j0; j < j1; ++j) local += seg_mass(j);
+        block_scan(local, excl, incl, total, sw);
     }
-    const double tt = pl.u2 * total;       // u2 < 1, so tt < total when total > 0
+    const double tt = pl.u2 * total;                   // u2 < 1: tt < total when total > 0
     if (t == 0) {
-        sSeg = -1;
-        sY = -1;
-    }
-    __syncthreads();
-    // The first segment whose running mass exceeds tt.  The thread holding it
-    // re-accumulates its own range exactly as `local` was formed, so the scan
-    // is certain to stop inside the range.
-    if (pre <= tt && pre + local > tt) {
-        double run = 0.0;
-        for (int j = j0; j < j1; ++j) {
-            const double before = run;
-            run += seg_mass(j, mode);
-            if (pre + run > tt || j == j1 - 1) {
-                sSeg = j;
-                sOff = pre + before;
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    if (sSeg < 0 && t == 0) {
-        // total == 0 (no mass anywhere): take the first segment.
         sSeg = 0;
         sOff = 0.0;
+        sY = -1;
+        sLastPos = -1;
+    }
+    __syncthreads();
+    // (b) the segment holding tt: exactly one thread has excl <= tt < incl.
+    if (excl <= tt && tt < incl) {
+        double run = excl;
+        int sel = -1, last = -1;
+        double sel_off = 0.0, last_off = 0.0;
+        for (int j = j0; j < j1; ++j) {
+            const double mj = seg_mass(j);
+            if (mj > 0.0) {
+                last = j;
+                last_off = run;
+            }
+            if (run + mj > tt) {
+                sel = j;
+                sel_off = run;
+                break;
+            }
+            run += mj;
+        }
+        if (sel < 0) {                                 // rounding: the range's last mass
+            sel = last < 0 ? j0 : last;
+            sel_off = last_off;
+        }
+        sSeg = sel;
+        sOff = sel_off;
     }
     __syncthreads();
     const int seg = sSeg;
-    const double tl = tt - sOff;
+    const double tl = fmax(0.0, tt - sOff);
 
-    // Re-read segment `seg`: thread t owns a contiguous run of elements.
-    const void *tp = row_ptr<DT>(target, tbs, trs, s, pl.slot);
-    const void *dp = row_ptr<DT>(draft, dbs, drs, s, mode == kModeResidual ? pl.slot : 0);
-    const int64_t E = seg_elems(DT) / kBlock;
-    const int64_t e0 = (int64_t)seg * seg_elems(DT) + (int64_t)t * E;
-    const int64_t e1 = min((int64_t)V, e0 + E);
-    auto weight = [&](int64_t e) -> float {
-        return mode == kModeResidual ? residual_weight(elem_at<DT>(tp, e), elem_at<DT>(dp, e), pl, c_hi, c_lo)
-                                     : target_weight(elem_at<DT>(tp, e), pl, c_hi, c_lo);
-    };
-    double wsum = 0.0;
-    for (int64_t e = e0; e < e1; ++e) wsum += (double)weight(e);
-    double segtotal = 0.0;
-    const double wpre = block_exclusive_prefix(wsum, sbuf, segtotal);
-    if (!(tl < segtotal)) {
-        // tl at or past this segment's recomputed total by rounding: the
-        // last positive weight of the segment is the one reached.
-        int64_t last_pos = -1;
-        for (int64_t e = e0; e < e1; ++e)
-            if (weight(e) > 0.0f) last_pos = e;
-        if (last_pos >= 0) atomicMax(&sY, (int32_t)last_pos);
-    } else if (wpre <= tl && wpre + wsum > tl) {
-        // Exactly one thread gets here; re-accumulating from zero in the same
-        // order reproduces wsum, so the scan stops inside the range.
-        double run = 0.0;
-        for (int64_t e = e0; e < e1; ++e) {
-            run += (double)weight(e);
-            if (wpre + run > tl) {
-                sY = (int32_t)e;
-                break;
-            }
-        }
+    // (c) re-read the segment and search it.
+    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
+    if (resid) {
+        const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
+        search_segment<DT, VEC, (int)(rseg_elems(DT) / kBlock), true>(
+            tp, dp, (int64_t)seg * rseg_elems(DT), V, pl, c_hi, c_lo, tl, sw, &sY, &sLastPos);
+    } else {
+        search_segment<DT, VEC, (int)(seg_elems(DT) / kBlock), false>(
+            tp, tp, (int64_t)seg * seg_elems(DT), V, pl, c_hi, c_lo, tl, sw, &sY, &sLastPos);
     }
     __syncthreads();
     if (t == 0) {
-        int32_t y = sY;
-        if (y < 0) y = (int32_t)min((int64_t)V - 1, (int64_t)seg * seg_elems(DT));
-        tokens[(int64_t)s * (K + 1) + pl.slot] = y;
+        int32_t y = sY >= 0 ? sY : sLastPos;
+        if (y < 0) y = (int32_t)min((int64_t)V - 1, (int64_t)seg * (resid ? rseg_elems(DT) : seg_elems(DT)));
+        c.tok[(int64_t)s * (K + 1) + pl.slot] = y;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+
+// Row pass: one single-wave workgroup per (row of the call, segment), rows
+// taken sequence by sequence, rps per sequence.  Draft rows of greedy
+// sequences and rows of invalid sequences are skipped.  (Single-wave
+// workgroups stream measurably faster on this part than 4-wave ones: a wave
+// starts as soon as one wave's resources free up.)
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
+    const int lane = threadIdx.x;
+    const int row = blockIdx.x / c.nseg;
+    const int seg = blockIdx.x - row * c.nseg;
+    const int s = row / c.rps, i = row - s * c.rps;
+    const double T = seq_temperature(c, s);
+    const int rule = rule_of(T);
+    if (rule == kRuleInvalid || (rule == kRuleGreedy && i > c.K)) return;
+    row_wave<DT, VEC>(c, s, i, seg, lane, rule, T);
+}
+
+// Scan of every sequence of the call: one 1024-thread block per sequence.
+template <int DT>
+__global__ __launch_bounds__(kScanBlock) void scan_kernel(Ctx c) {
+    scan_seq<DT, kScanBlock / kWave>(c, blockIdx.x);
+}
+
+// Residual pass: one single-wave workgroup per (sequence, residual segment).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void residual_kernel(Ctx c) {
+    const int s = blockIdx.x / c.nres;
+    const int seg = blockIdx.x - s * c.nres;
+    residual_wave<DT, VEC>(c, s, seg, threadIdx.x);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void draw_kernel(Ctx c) {
+    draw_seq<DT, VEC>(c, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -698,7 +893,7 @@ __global__ __launch_bounds__(kBlock) void stream_copy_kernel(uint4 *__restrict__
 #pragma unroll
     for (int u = 0; u < kVecPerLane; ++u) {
         int64_t vi = base + u * kBlock + threadIdx.x;
-        if (vi < nvec) d[u] = src[vi];
+        if (vi < nvec) d[u] = load_stream(src + vi);
     }
 #pragma unroll
     for (int u = 0; u < kVecPerLane; ++u) {
@@ -713,32 +908,33 @@ __global__ __launch_bounds__(kBlock) void stream_copy_kernel(uint4 *__restrict__
 thread_local hipEvent_t *t_stage_events = nullptr;
 thread_local int t_stage_n = 0;
 
-inline void stage_mark(int k, int nkernels, hipStream_t st) {
-    if (t_stage_events && t_stage_n >= nkernels + 1) (void)hipEventRecord(t_stage_events[k], st);
+// Profiling marks never fail a call: an event-record error is cleared here so
+// it cannot surface at the next launch check.
+inline void stage_mark(int k, hipStream_t st) {
+    if (t_stage_events && k < t_stage_n) {
+        if (hipEventRecord(t_stage_events[k], st) != hipSuccess) (void)hipGetLastError();
+    }
 }
 
+enum : int { kCallGreedy = 0, kCallSample = 1, kCallMixed = 2 };
+
 struct Layout {
-    int nseg;
-    size_t part_off, part_bytes;
-    size_t plan_off, plan_bytes;
-    size_t rmass_off, rmass_bytes;
-    size_t total;
+    int nseg, nres, rps;
+    size_t part_off, plan_off, rmass_off, total;
 };
 
-bool make_layout(int b, int K, int V, int dtype, int sampling, Layout &L) {
-    if (b < 1 || K < 1 || K > SPEC_MAX_K || V < 1) return false;
+bool make_layout(int b, int K, int V, int dtype, int kind, Layout &L) {
+    if (b < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > INT_MAX - 65536) return false;
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return false;
-    const int64_t se = seg_elems(dtype);
-    L.nseg = (int)(((int64_t)V + se - 1) / se);
-    const int64_t rows = sampling ? (int64_t)b * (2 * K + 1) : (int64_t)b * (K + 1);
-    const size_t psize = sampling ? sizeof(SamplePartial) : sizeof(GreedyPartial);
+    if (kind != kCallGreedy && kind != kCallSample && kind != kCallMixed) return false;
+    L.nseg = (int)(((int64_t)V + seg_elems(dtype) - 1) / seg_elems(dtype));
+    L.nres = (int)(((int64_t)V + rseg_elems(dtype) - 1) / rseg_elems(dtype));
+    L.rps = kind == kCallGreedy ? K + 1 : 2 * K + 1;
+    const bool draws = kind != kCallGreedy;
     L.part_off = 0;
-    L.part_bytes = align256((size_t)rows * (size_t)L.nseg * psize);
-    L.plan_off = L.part_off + L.part_bytes;
-    L.plan_bytes = sampling ? align256((size_t)b * sizeof(DrawPlan)) : 0;
-    L.rmass_off = L.plan_off + L.plan_bytes;
-    L.rmass_bytes = sampling ? align256((size_t)b * (size_t)L.nseg * sizeof(double)) : 0;
-    L.total = L.rmass_off + L.rmass_bytes;
+    L.plan_off = L.part_off + align256((size_t)b * L.rps * (size_t)L.nseg * sizeof(Partial));
+    L.rmass_off = L.plan_off + (draws ? align256((size_t)b * sizeof(DrawPlan)) : 0);
+    L.total = L.rmass_off + (draws ? align256((size_t)b * (size_t)L.nres * sizeof(double)) : 0);
     return true;
 }
 
@@ -746,66 +942,44 @@ bool rows_vector_aligned(const void *p, int es, int64_t bs, int64_t rs) {
     return ((uintptr_t)p % 16 == 0) && ((bs * es) % 16 == 0) && ((rs * es) % 16 == 0);
 }
 
-// log2(e)/T as hi + lo with hi rounded down and lo >= FLT_MIN.
-void split_scale(double T, float &c_hi, float &c_lo, double &c64) {
-    c64 = 1.4426950408889634 / T;
-    float hi = (float)c64;
-    if ((double)hi > c64) hi = nextafterf(hi, 0.0f);
-    double lo = c64 - (double)hi;
-    c_hi = hi;
-    c_lo = (float)lo < FLT_MIN ? FLT_MIN : (float)lo;
-}
-
 template <int DT, bool VEC>
-int launch_greedy(const void *target, int64_t bs, int64_t rs, const int32_t *x, int b, int K, int V,
-                  int32_t *n_out, int32_t *tok, int32_t *am, char *ws, const Layout &L, hipStream_t st) {
-    const int seg_blocks = (L.nseg + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t grid = (int64_t)b * (K + 1) * seg_blocks;
-    if (grid > INT_MAX) return SPEC_EINVAL;
-    GreedyPartial *part = (GreedyPartial *)(ws + L.part_off);
-    stage_mark(0, 2, st);
-    hipLaunchKernelGGL((row_stats_greedy<DT, VEC>), dim3((unsigned)grid), dim3(kBlock), 0, st,
-                       target, bs, rs, K + 1, V, L.nseg, seg_blocks, part);
+int launch(const Ctx &c, int b, int kind, const Layout &L, hipStream_t st) {
+    const int64_t grid_rows = (int64_t)b * L.rps * L.nseg;
+    const int64_t grid_res = (int64_t)b * L.nres;
+    if (grid_rows > INT_MAX || grid_res > INT_MAX) return SPEC_EINVAL;
+    stage_mark(0, st);
+    hipLaunchKernelGGL((row_pass<DT, VEC>), dim3((unsigned)grid_rows), dim3(kWave), 0, st, c);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(1, 2, st);
-    hipLaunchKernelGGL(scan_greedy, dim3((unsigned)b), dim3(kWave), 0, st, part, L.nseg, K, V, x, n_out, tok, am);
+    stage_mark(1, st);
+    hipLaunchKernelGGL((scan_kernel<DT>), dim3((unsigned)b), dim3(kScanBlock), 0, st, c);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(2, 2, st);
+    stage_mark(2, st);
+    if (kind == kCallGreedy) return SPEC_OK;
+    hipLaunchKernelGGL((residual_kernel<DT, VEC>), dim3((unsigned)grid_res), dim3(kWave), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(3, st);
+    hipLaunchKernelGGL((draw_kernel<DT, VEC>), dim3((unsigned)b), dim3(kBlock), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(4, st);
     return SPEC_OK;
 }
 
-template <int DT, bool VEC>
-int launch_sample(const void *target, const void *draft, int64_t tbs, int64_t trs, int64_t dbs, int64_t drs,
-                  const int32_t *x, int b, int K, int V, double T, const uint64_t *seeds, int32_t *n_out,
-                  int32_t *tok, float *p_out, float *q_out, char *ws, const Layout &L, hipStream_t st) {
-    const int seg_blocks = (L.nseg + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t grid1 = (int64_t)b * (2 * K + 1) * seg_blocks;
-    const int64_t grid3 = (int64_t)b * seg_blocks;
-    if (grid1 > INT_MAX) return SPEC_EINVAL;
-    float c_hi, c_lo;
-    double c64;
-    split_scale(T, c_hi, c_lo, c64);
-    SamplePartial *part = (SamplePartial *)(ws + L.part_off);
-    DrawPlan *plan = (DrawPlan *)(ws + L.plan_off);
-    double *rmass = (double *)(ws + L.rmass_off);
-    stage_mark(0, 4, st);
-    hipLaunchKernelGGL((row_stats_sample<DT, VEC>), dim3((unsigned)grid1), dim3(kBlock), 0, st,
-                       target, draft, tbs, trs, dbs, drs, K, V, L.nseg, seg_blocks, c_hi, c_lo, c64, part);
-    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(1, 4, st);
-    hipLaunchKernelGGL((scan_sample<DT>), dim3((unsigned)b), dim3(kWave), 0, st, part, L.nseg, K, V, T, c64,
-                       target, draft, tbs, trs, dbs, drs, x, seeds, n_out, tok, p_out, q_out, plan);
-    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(2, 4, st);
-    hipLaunchKernelGGL((residual_mass<DT, VEC>), dim3((unsigned)grid3), dim3(kBlock), 0, st,
-                       target, draft, tbs, trs, dbs, drs, V, L.nseg, seg_blocks, c_hi, c_lo, plan, rmass);
-    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(3, 4, st);
-    hipLaunchKernelGGL((draw_token<DT>), dim3((unsigned)b), dim3(kBlock), 0, st, target, draft, tbs, trs, dbs,
-                       drs, K, V, L.nseg, c_hi, c_lo, c64, part, rmass, plan, tok);
-    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-    stage_mark(4, 4, st);
-    return SPEC_OK;
+// Fills the workspace pointers of `c` and launches the call's kernels.
+int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L, hipStream_t st) {
+    char *ws = (char *)workspace;
+    c.nseg = L.nseg;
+    c.nres = L.nres;
+    c.rps = L.rps;
+    c.part = (Partial *)(ws + L.part_off);
+    const bool draws = kind != kCallGreedy;
+    c.plan = draws ? (DrawPlan *)(ws + L.plan_off) : nullptr;
+    c.rmass = draws ? (double *)(ws + L.rmass_off) : nullptr;
+    const int es = elem_bytes(dtype);
+    bool vec = rows_vector_aligned(c.target, es, c.tbs, c.trs);
+    if (kind != kCallGreedy) vec = vec && rows_vector_aligned(c.draft, es, c.dbs, c.drs);
+    if (dtype == SPEC_BF16)
+        return vec ? launch<SPEC_BF16, true>(c, b, kind, L, st) : launch<SPEC_BF16, false>(c, b, kind, L, st);
+    return vec ? launch<SPEC_F32, true>(c, b, kind, L, st) : launch<SPEC_F32, false>(c, b, kind, L, st);
 }
 
 }  // namespace
@@ -814,7 +988,13 @@ extern "C" {
 
 size_t spec_workspace_bytes(int b, int K, int V, int dtype, int sampling) {
     Layout L;
-    if (!make_layout(b, K, V, dtype, sampling, L)) return 0;
+    if (!make_layout(b, K, V, dtype, sampling ? kCallSample : kCallGreedy, L)) return 0;
+    return L.total;
+}
+
+size_t spec_mixed_workspace_bytes(int b, int K, int V, int dtype) {
+    Layout L;
+    if (!make_layout(b, K, V, dtype, kCallMixed, L)) return 0;
     return L.total;
 }
 
@@ -841,24 +1021,23 @@ int spec_greedy_accept(const void *target, int dtype, int64_t t_batch_stride, in
                        void *hip_stream) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
     Layout L;
-    if (!make_layout(b, K, V, dtype, 0, L)) return SPEC_EINVAL;
+    if (!make_layout(b, K, V, dtype, kCallGreedy, L)) return SPEC_EINVAL;
     if (!target || !draft_tokens || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0) return SPEC_EINVAL;
     if (workspace_bytes < L.total) return SPEC_EINVAL;
-    const int es = elem_bytes(dtype);
-    if ((uintptr_t)target % es != 0) return SPEC_EALIGN;
-    hipStream_t st = (hipStream_t)hip_stream;
-    const bool vec = rows_vector_aligned(target, es, t_batch_stride, t_row_stride);
-    char *ws = (char *)workspace;
-    if (dtype == SPEC_BF16)
-        return vec ? launch_greedy<SPEC_BF16, true>(target, t_batch_stride, t_row_stride, draft_tokens, b, K, V,
-                                                     n_accepted, tokens, target_argmax, ws, L, st)
-                   : launch_greedy<SPEC_BF16, false>(target, t_batch_stride, t_row_stride, draft_tokens, b, K, V,
-                                                      n_accepted, tokens, target_argmax, ws, L, st);
-    return vec ? launch_greedy<SPEC_F32, true>(target, t_batch_stride, t_row_stride, draft_tokens, b, K, V,
-                                                n_accepted, tokens, target_argmax, ws, L, st)
-               : launch_greedy<SPEC_F32, false>(target, t_batch_stride, t_row_stride, draft_tokens, b, K, V,
-                                                 n_accepted, tokens, target_argmax, ws, L, st);
+    if ((uintptr_t)target % elem_bytes(dtype) != 0) return SPEC_EALIGN;
+    Ctx c = {};
+    c.target = target;
+    c.tbs = t_batch_stride;
+    c.trs = t_row_stride;
+    c.K = K;
+    c.V = V;
+    c.T_uniform = 0.0;
+    c.x = draft_tokens;
+    c.n_out = n_accepted;
+    c.tok = tokens;
+    c.am = target_argmax;
+    return dispatch(c, b, workspace, dtype, kCallGreedy, L, (hipStream_t)hip_stream);
 }
 
 int spec_sample_accept(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
@@ -868,30 +1047,65 @@ int spec_sample_accept(const void *target, const void *draft, int dtype, int64_t
                        float *q_draft, void *workspace, size_t workspace_bytes, void *hip_stream) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
     Layout L;
-    if (!make_layout(b, K, V, dtype, 1, L)) return SPEC_EINVAL;
+    if (!make_layout(b, K, V, dtype, kCallSample, L)) return SPEC_EINVAL;
     if (!target || !draft || !draft_tokens || !seeds || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
     if (!(temperature > 0.0) || !(temperature < INFINITY)) return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0 || d_row_stride < V || d_batch_stride < 0) return SPEC_EINVAL;
     if (workspace_bytes < L.total) return SPEC_EINVAL;
     const int es = elem_bytes(dtype);
     if ((uintptr_t)target % es != 0 || (uintptr_t)draft % es != 0) return SPEC_EALIGN;
-    hipStream_t st = (hipStream_t)hip_stream;
-    const bool vec = rows_vector_aligned(target, es, t_batch_stride, t_row_stride) &&
-                     rows_vector_aligned(draft, es, d_batch_stride, d_row_stride);
-    char *ws = (char *)workspace;
-    if (dtype == SPEC_BF16)
-        return vec ? launch_sample<SPEC_BF16, true>(target, draft, t_batch_stride, t_row_stride, d_batch_stride,
-                                                     d_row_stride, draft_tokens, b, K, V, temperature, seeds,
-                                                     n_accepted, tokens, p_draft, q_draft, ws, L, st)
-                   : launch_sample<SPEC_BF16, false>(target, draft, t_batch_stride, t_row_stride, d_batch_stride,
-                                                      d_row_stride, draft_tokens, b, K, V, temperature, seeds,
-                                                      n_accepted, tokens, p_draft, q_draft, ws, L, st);
-    return vec ? launch_sample<SPEC_F32, true>(target, draft, t_batch_stride, t_row_stride, d_batch_stride,
-                                                d_row_stride, draft_tokens, b, K, V, temperature, seeds, n_accepted,
-                                                tokens, p_draft, q_draft, ws, L, st)
-               : launch_sample<SPEC_F32, false>(target, draft, t_batch_stride, t_row_stride, d_batch_stride,
-                                                 d_row_stride, draft_tokens, b, K, V, temperature, seeds, n_accepted,
-                                                 tokens, p_draft, q_draft, ws, L, st);
+    Ctx c = {};
+    c.target = target;
+    c.draft = draft;
+    c.tbs = t_batch_stride;
+    c.trs = t_row_stride;
+    c.dbs = d_batch_stride;
+    c.drs = d_row_stride;
+    c.K = K;
+    c.V = V;
+    c.T_uniform = temperature;
+    c.x = draft_tokens;
+    c.seeds = seeds;
+    c.n_out = n_accepted;
+    c.tok = tokens;
+    c.p_out = p_draft;
+    c.q_out = q_draft;
+    return dispatch(c, b, workspace, dtype, kCallSample, L, (hipStream_t)hip_stream);
+}
+
+int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
+                      int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
+                      const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
+                      const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, float *p_draft,
+                      float *q_draft, int32_t *target_argmax, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
+    Layout L;
+    if (!make_layout(b, K, V, dtype, kCallMixed, L)) return SPEC_EINVAL;
+    if (!target || !draft || !draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace)
+        return SPEC_EINVAL;
+    if (t_row_stride < V || t_batch_stride < 0 || d_row_stride < V || d_batch_stride < 0) return SPEC_EINVAL;
+    if (workspace_bytes < L.total) return SPEC_EINVAL;
+    const int es = elem_bytes(dtype);
+    if ((uintptr_t)target % es != 0 || (uintptr_t)draft % es != 0) return SPEC_EALIGN;
+    Ctx c = {};
+    c.target = target;
+    c.draft = draft;
+    c.tbs = t_batch_stride;
+    c.trs = t_row_stride;
+    c.dbs = d_batch_stride;
+    c.drs = d_row_stride;
+    c.K = K;
+    c.V = V;
+    c.temps = temperatures;
+    c.x = draft_tokens;
+    c.seeds = seeds;
+    c.n_out = n_accepted;
+    c.tok = tokens;
+    c.p_out = p_draft;
+    c.q_out = q_draft;
+    c.am = target_argmax;
+    return dispatch(c, b, workspace, dtype, kCallMixed, L, (hipStream_t)hip_stream);
 }
 
 int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream) {

@@ -87,10 +87,10 @@ def compare_greedy(case: W.Case, n_g, tok_g, am_g, name: str) -> Report:
     return rep
 
 
-def _draw_near_tie(case: W.Case, res: dict, s: int, slot: int, y_g: int) -> bool:
+def _draw_near_tie(case: W.Case, res: dict, s: int, slot: int, y_g: int, T: float) -> bool:
     if y_g < 0 or y_g >= case.V:
         return False
-    F = oracle.draw_cdf(case.target, case.draft, case.T, s, slot, bool(res["residual"][s]))
+    F = oracle.draw_cdf(case.target, case.draft, T, s, slot, bool(res["residual"][s]))
     t, R, y_o = res["t"][s], res["R"][s], res["tokens"][s, slot]
     if y_g > y_o:
         margin = F[y_g - 1] - t
@@ -99,13 +99,20 @@ def _draw_near_tie(case: W.Case, res: dict, s: int, slot: int, y_g: int) -> bool
     return 0.0 <= margin <= DRAW_BAND * R
 
 
-def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str) -> Report:
-    res = oracle.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
+def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str, res: dict = None,
+                   temps=None) -> Report:
+    """Sampling sequences of `case` (all of them, or those with temps > 0)."""
+    if res is None:
+        res = oracle.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
+    if temps is None:
+        temps = np.full(case.b, case.T)
+    seqs = [s for s in range(case.b) if temps[s] != 0.0]
     n_o, tok_o = res["n_accepted"], res["tokens"]
-    rep = Report(sequences=case.b, sampling_sequences=case.b)
+    rep = Report(sequences=len(seqs), sampling_sequences=len(seqs))
     K = case.K
-    band = np.abs(res["u"] - np.minimum(1.0, res["r"])) < ACCEPT_BAND
-    for s in range(case.b):
+    with np.errstate(invalid="ignore"):
+        band = np.abs(res["u"] - np.minimum(1.0, res["r"])) < ACCEPT_BAND
+    for s in seqs:
         # probabilities of every slot
         if n_o[s] >= 0:
             for arr_g, arr_o in ((p_g, res["p_draft"]), (q_g, res["q_draft"])):
@@ -141,12 +148,46 @@ def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str) -> Report:
             continue
         n = int(n_o[s])
         if (tok_g[s, :n] == tok_o[s, :n]).all() and (tok_g[s, n + 1:] == -1).all() and \
-                _draw_near_tie(case, res, s, n, int(tok_g[s, n])):
+                _draw_near_tie(case, res, s, n, int(tok_g[s, n]), float(temps[s])):
             rep.draw_near_tie_mismatch += 1
             continue
         rep.failures.append(dict(case=name, seq=s, what="tokens", n=n, tok_gpu=tok_g[s].tolist(),
                                  tok_oracle=tok_o[s].tolist(), t=float(res["t"][s]), R=float(res["R"][s])))
     return rep
+
+
+def compare_mixed(case: W.Case, temps: np.ndarray, n_g, tok_g, p_g, q_g, am_g, name: str) -> Report:
+    res = oracle.mixed_accept(case.target, case.draft, case.draft_tokens, temps, case.seeds)
+    rep = compare_sample(case, n_g, tok_g, p_g, q_g, name, res=res, temps=temps)
+    greedy = np.nonzero(temps == 0.0)[0]
+    rep.sequences += len(greedy)
+    rep.greedy_sequences += len(greedy)
+    for s in greedy:
+        ok = (n_g[s] == res["n_accepted"][s] and (tok_g[s] == res["tokens"][s]).all()
+              and (am_g[s] == res["argmax"][s]).all() and np.isnan(p_g[s]).all() and np.isnan(q_g[s]).all())
+        if ok:
+            rep.exact_sequences += 1
+        else:
+            rep.failures.append(dict(case=name, seq=int(s), what="greedy in mixed", n_gpu=int(n_g[s]),
+                                     n_oracle=int(res["n_accepted"][s]), tok_gpu=tok_g[s].tolist(),
+                                     tok_oracle=res["tokens"][s].tolist()))
+    sampling = np.nonzero(temps != 0.0)[0]
+    if not (am_g[sampling] == -1).all():
+        rep.failures.append(dict(case=name, what="argmax of sampling sequences must be -1"))
+    return rep
+
+
+def run_gpu_mixed(case: W.Case, temps: np.ndarray, target_dev=None, draft_dev=None):
+    import lossless_draft_verification_amd as L
+    t = to_device(case.target) if target_dev is None else target_dev
+    d = to_device(case.draft) if draft_dev is None else draft_dev
+    x = torch.from_numpy(case.draft_tokens).cuda()
+    sd = seeds_to_device(case.seeds)
+    T = torch.from_numpy(np.ascontiguousarray(temps, dtype=np.float64)).cuda()
+    r = L.mixed_accept(t, d, x, T, sd)
+    torch.cuda.synchronize()
+    return (r.n_accepted.cpu().numpy(), r.tokens.cpu().numpy(), r.p_draft.cpu().numpy(),
+            r.q_draft.cpu().numpy(), r.argmax.cpu().numpy())
 
 
 def run_gpu_greedy(case: W.Case, target_dev=None):

@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import workloads as W
-from parity import (Report, compare_greedy, compare_sample, run_gpu_greedy, run_gpu_sample,
-                    to_device, seeds_to_device)
+from parity import (Report, compare_greedy, compare_mixed, compare_sample, run_gpu_greedy,
+                    run_gpu_mixed, run_gpu_sample, to_device, seeds_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +175,44 @@ def test_workload_c5_split_calls():
     rep.merge(compare_sample(case.take(s), rs.n_accepted.cpu().numpy(), rs.tokens.cpu().numpy(),
                              rs.p_draft.cpu().numpy(), rs.q_draft.cpu().numpy(), "c5_sample"))
     _check(rep, "workload_c5")
+
+
+# ------------------------------------------------------------ mixed batches
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mixed_small(dtype):
+    """Per-sequence temperatures: greedy (0), several sampling temperatures and
+    invalid values (negative, NaN, inf) in one batch."""
+    b = 12
+    case = W.make_case("mixed", b=b, K=4, V=20000, dtype=dtype, target_scale=2.5,
+                       draft_sigma=(0.2, 1.5), T=0.8, seed=31)
+    temps = np.array([0.0, 0.8, 1.0, 0.0, 0.5, 2.0, 0.0, 0.8, -1.0, np.nan, np.inf, 0.7])
+    out = run_gpu_mixed(case, temps)
+    n = out[0]
+    assert (n[[8, 9, 10]] == -1).all() and (n[[0, 1, 2, 3, 4, 5, 6, 7, 11]] >= 0).all()
+    _check(compare_mixed(case, temps, *out, f"mixed_small_{dtype}"), f"mixed_small_{dtype}")
+
+
+def test_mixed_matches_single_rule_calls():
+    """A mixed batch whose sequences all share one rule equals the single-rule
+    entry point bit for bit (same Philox rows)."""
+    case = W.make_case("mix1", b=9, K=7, V=40000, dtype="bf16", target_scale=3.0,
+                       draft_sigma=(0.1, 2.0), T=0.8, seed=41)
+    m = run_gpu_mixed(case, np.full(case.b, 0.8))
+    s = run_gpu_sample(case)
+    for a, b_ in zip(m[:4], s):
+        np.testing.assert_array_equal(a, b_)
+    g = run_gpu_mixed(case, np.zeros(case.b))
+    gg = run_gpu_greedy(case)
+    np.testing.assert_array_equal(g[0], gg[0])
+    np.testing.assert_array_equal(g[1], gg[1])
+    np.testing.assert_array_equal(g[4], gg[2])
+
+
+def test_workload_c5_mixed_call():
+    """b=128, K=7, V=262144 bf16 with rows 0..63 greedy and 64..127 sampling at
+    T=0.8 in ONE mixed call (Philox rows are the batch indices 0..127)."""
+    case = W.config(5)
+    temps = np.where(case.rule == W.GREEDY, 0.0, case.T)
+    _check(compare_mixed(case, temps, *run_gpu_mixed(case, temps), "c5_mixed"), "workload_c5_mixed")

@@ -72,7 +72,7 @@ class Oracle:
                                              dbl, vp, vp, vp, vp, vp, vp]
         lib.oracle_sample_accept.restype = i32
         lib.oracle_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32,
-                                            vp, vp, vp, vp, vp, vp, vp, vp]
+                                            vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_mixed_accept.restype = i32
         lib.oracle_draw_cdf.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, i32, dbl,
                                         i32, i32, i32, vp]
@@ -155,9 +155,10 @@ class Oracle:
         }
 
     def mixed_accept(self, target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
-                     temperatures: np.ndarray, seeds: np.ndarray) -> dict:
+                     temperatures: np.ndarray, seeds: np.ndarray, draft_lengths=None) -> dict:
         """Mixed batch: greedy where temperatures[s] == 0, sampling at
-        temperatures[s] > 0.  Same outputs as sample_accept plus argmax."""
+        temperatures[s] > 0; sequence s uses draft_lengths[s] <= K draft
+        tokens (all K when None).  Same outputs as sample_accept plus argmax."""
         target = np.ascontiguousarray(target)
         draft = np.ascontiguousarray(draft)
         x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
@@ -173,8 +174,13 @@ class Oracle:
         q = np.zeros((b, K), np.float64)
         am = np.zeros((b, K + 1), np.int32)
         diag = np.zeros((b, 2 * K + 4), np.float64)
+        lens = None
+        if draft_lengths is not None:
+            lens = np.ascontiguousarray(draft_lengths, dtype=np.int32)
+            assert lens.shape == (b,)
         rc = self.lib.oracle_mixed_accept(_ptr(target), _ptr(draft), _dtype_code(target),
                                           K1 * V, V, K * V, V, _ptr(x), b, K, V, _ptr(temps),
+                                          _ptr(lens) if lens is not None else None,
                                           _ptr(seeds), _ptr(n), _ptr(tok), _ptr(p), _ptr(q),
                                           _ptr(am), _ptr(diag))
         if rc != 0:
@@ -233,8 +239,8 @@ def sample_accept(target, draft, draft_tokens, temperature, seeds):
     return default().sample_accept(target, draft, draft_tokens, temperature, seeds)
 
 
-def mixed_accept(target, draft, draft_tokens, temperatures, seeds):
-    return default().mixed_accept(target, draft, draft_tokens, temperatures, seeds)
+def mixed_accept(target, draft, draft_tokens, temperatures, seeds, draft_lengths=None):
+    return default().mixed_accept(target, draft, draft_tokens, temperatures, seeds, draft_lengths)
 
 
 def draw_cdf(target, draft, temperature, s, slot, residual):

@@ -186,16 +186,22 @@ static double row_log_normaliser(const void *base, int dtype, int64_t off,
 /* For each sequence: A_i = argmax of target row i (i = 0..K); n = length of  */
 /* the longest prefix with x_i == A_i; committed tokens x_0..x_{n-1}, A_n,    */
 /* then -1 up to K+1 entries.                                                */
+/* A sequence may carry only Ks <= K draft tokens (a shorter block): then     */
+/* rows 0..Ks and tokens 0..Ks-1 are its block, row Ks its bonus position,    */
+/* and the rest of its [K+1] / [K] storage is not read.  K is the stride.     */
 
 static void greedy_sequence(const void *target, int dtype,
                             int64_t t_batch_stride, int64_t t_row_stride,
-                            const int32_t *draft_tokens, int s, int K, int V,
+                            const int32_t *draft_tokens, int s, int K, int Ks, int V,
                             int32_t *n_accepted, int32_t *tokens,
                             int32_t *target_argmax)
 {
     int valid = 1;
     int32_t *A = (int32_t *)calloc((size_t)(K + 1), sizeof(int32_t));
     for (int i = 0; i <= K; ++i) {
+        A[i] = -1;
+    }
+    for (int i = 0; i <= Ks; ++i) {
         int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
         if (!row_is_valid(target, dtype, off, V)) {
             valid = 0;
@@ -204,7 +210,7 @@ static void greedy_sequence(const void *target, int dtype,
             A[i] = row_argmax(target, dtype, off, V);
         }
     }
-    for (int i = 0; i < K; ++i) {
+    for (int i = 0; i < Ks; ++i) {
         int32_t x = draft_tokens[(int64_t)s * K + i];
         if (x < 0 || x >= V) {
             valid = 0;
@@ -225,7 +231,7 @@ static void greedy_sequence(const void *target, int dtype,
         return;
     }
     int n = 0;
-    while (n < K && draft_tokens[(int64_t)s * K + n] == A[n]) {
+    while (n < Ks && draft_tokens[(int64_t)s * K + n] == A[n]) {
         ++n;
     }
     for (int j = 0; j < n; ++j) {
@@ -246,7 +252,7 @@ int oracle_greedy_accept(const void *target, int dtype,
         return 1;
     }
     for (int s = 0; s < b; ++s) {
-        greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, V,
+        greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, K, V,
                         n_accepted, tokens, target_argmax);
     }
     return 0;
@@ -290,7 +296,7 @@ static double draw_weight(const void *target, const void *draft, int dtype,
 static void sample_sequence(const void *target, const void *draft, int dtype,
                             int64_t t_batch_stride, int64_t t_row_stride,
                             int64_t d_batch_stride, int64_t d_row_stride,
-                            const int32_t *draft_tokens, int s, int K, int V,
+                            const int32_t *draft_tokens, int s, int K, int Ks, int V,
                             double T, const uint64_t *seeds,
                             int32_t *n_accepted, int32_t *tokens,
                             double *p_draft, double *q_draft, double *diag)
@@ -301,16 +307,25 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     for (int j = 0; j <= K; ++j) {
         tok[j] = -1;
     }
+    for (int i = 0; i < K; ++i) {          /* slots past the block report NaN */
+        p_draft[(int64_t)s * K + i] = NAN;
+        q_draft[(int64_t)s * K + i] = NAN;
+    }
+    if (diag) {
+        for (int j = 0; j < dstride; ++j) {
+            diag[(int64_t)s * dstride + j] = NAN;
+        }
+    }
     int valid = 1;
-    for (int i = 0; i <= K && valid; ++i) {
+    for (int i = 0; i <= Ks && valid; ++i) {
         int64_t off = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
         valid = row_is_valid(target, dtype, off, V);
     }
-    for (int i = 0; i < K && valid; ++i) {
+    for (int i = 0; i < Ks && valid; ++i) {
         int64_t off = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
         valid = row_is_valid(draft, dtype, off, V);
     }
-    for (int i = 0; i < K; ++i) {
+    for (int i = 0; i < Ks; ++i) {
         if (x[i] < 0 || x[i] >= V) {
             valid = 0;
         }
@@ -331,8 +346,8 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
 
     /* Step 1: log-normalisers of every target and draft row. */
     double *Ct = (double *)malloc(sizeof(double) * (size_t)(K + 1));
-    double *Cd = (double *)malloc(sizeof(double) * (size_t)K);
-    for (int i = 0; i <= K; ++i) {
+    double *Cd = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    for (int i = 0; i <= Ks; ++i) {
         Ct[i] = row_log_normaliser(target, dtype,
                                    (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride,
                                    V, T);
@@ -342,16 +357,16 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
 #else
     const double Tq = T;
 #endif
-    for (int i = 0; i < K; ++i) {
+    for (int i = 0; i < Ks; ++i) {
         Cd[i] = row_log_normaliser(draft, dtype,
                                    (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride,
                                    V, Tq);
     }
 
     /* Step 2: accept test of every slot, stopping the prefix at the first
-     * rejection; ratios and probabilities are reported for all K slots. */
-    int n = K;
-    for (int i = 0; i < K; ++i) {
+     * rejection; ratios and probabilities are reported for all Ks slots. */
+    int n = Ks;
+    for (int i = 0; i < Ks; ++i) {
         int64_t toff = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
         int64_t doff = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
         double lp = logit_at(target, dtype, toff + x[i]) / T - Ct[i];
@@ -373,21 +388,22 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
             diag[(int64_t)s * dstride + K + i] = u;
         }
         double accept_prob = r < 1.0 ? r : 1.0;
-        if (n == K && !(u < accept_prob)) {
+        if (n == Ks && !(u < accept_prob)) {
             n = i;
         }
     }
 
-    /* Step 3: draw the token at slot n: residual when n < K, bonus from
-     * p_{K+1} when n == K; inverse CDF in ascending vocabulary order. */
+    /* Step 3: draw the token at slot n: residual when n < Ks, bonus from
+     * the block's last row when n == Ks; inverse CDF in ascending vocabulary
+     * order. */
 #if ORACLE_MUTANT == 3
-    const int draw_row = n < K ? n : K - 1;
+    const int draw_row = n < Ks ? n : (Ks > 0 ? Ks - 1 : 0);
 #else
     const int draw_row = n;
 #endif
     int64_t toff = (int64_t)s * t_batch_stride + (int64_t)draw_row * t_row_stride;
-    int64_t doff = (int64_t)s * d_batch_stride + (int64_t)(n < K ? n : 0) * d_row_stride;
-    int residual = n < K;
+    int64_t doff = (int64_t)s * d_batch_stride + (int64_t)(n < Ks ? n : 0) * d_row_stride;
+    int residual = n < Ks;
     double Cdn = residual ? Cd[n] : 0.0;
     double R = 0.0;
     for (int v = 0; v < V; ++v) {
@@ -448,7 +464,7 @@ int oracle_sample_accept(const void *target, const void *draft, int dtype,
     }
     for (int s = 0; s < b; ++s) {
         sample_sequence(target, draft, dtype, t_batch_stride, t_row_stride,
-                        d_batch_stride, d_row_stride, draft_tokens, s, K, V, T, seeds,
+                        d_batch_stride, d_row_stride, draft_tokens, s, K, K, V, T, seeds,
                         n_accepted, tokens, p_draft, q_draft, diag);
     }
     return 0;
@@ -461,12 +477,20 @@ int oracle_sample_accept(const void *target, const void *draft, int dtype,
  * sequence invalid.  Each sequence gets exactly what the single-rule
  * functions compute for it, with its index s in this batch as the Philox
  * row.  Greedy sequences report NaN probabilities; sampling sequences report
- * -1 argmax entries. */
+ * -1 argmax entries.
+ * draft_lengths (or NULL: all K): sequence s uses only Ks = draft_lengths[s]
+ * draft tokens, 0 <= Ks <= K -- the adaptive block length of a confidence
+ * head, or a --max-draft cap ("mlx-dspark 0.0.1" sdist diff, README "Tuning";
+ * __main__.py flags --max-draft and --confidence-threshold).  Its block is
+ * then target rows 0..Ks (row Ks the bonus position) and draft rows
+ * 0..Ks-1; Ks = 0 is a plain decode step.  Ks outside [0, K] makes the
+ * sequence invalid. */
 int oracle_mixed_accept(const void *target, const void *draft, int dtype,
                         int64_t t_batch_stride, int64_t t_row_stride,
                         int64_t d_batch_stride, int64_t d_row_stride,
                         const int32_t *draft_tokens, int b, int K, int V,
-                        const double *temps, const uint64_t *seeds,
+                        const double *temps, const int32_t *draft_lengths,
+                        const uint64_t *seeds,
                         int32_t *n_accepted, int32_t *tokens,
                         double *p_draft, double *q_draft, int32_t *target_argmax,
                         double *diag)
@@ -477,14 +501,16 @@ int oracle_mixed_accept(const void *target, const void *draft, int dtype,
     const int dstride = 2 * K + 4;
     for (int s = 0; s < b; ++s) {
         const double T = temps[s];
-        const int greedy = T == 0.0;
-        const int sampling = T > 0.0 && !isinf(T);
+        const int Ks = draft_lengths ? draft_lengths[s] : K;
+        const int len_ok = Ks >= 0 && Ks <= K;
+        const int greedy = len_ok && T == 0.0;
+        const int sampling = len_ok && T > 0.0 && !isinf(T);
         if (greedy) {
-            greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, V,
+            greedy_sequence(target, dtype, t_batch_stride, t_row_stride, draft_tokens, s, K, Ks, V,
                             n_accepted, tokens, target_argmax);
         } else if (sampling) {
             sample_sequence(target, draft, dtype, t_batch_stride, t_row_stride,
-                            d_batch_stride, d_row_stride, draft_tokens, s, K, V, T, seeds,
+                            d_batch_stride, d_row_stride, draft_tokens, s, K, Ks, V, T, seeds,
                             n_accepted, tokens, p_draft, q_draft, diag);
         } else {
             n_accepted[s] = -1;

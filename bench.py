@@ -213,6 +213,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--step", choices=["mixed", "split"], default="mixed")
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--ragged", action="store_true",
+                    help="mixed step with per-sequence draft lengths drawn uniformly from 0..K")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference", action="store_true", help="skip the split-call reference region")
@@ -222,6 +224,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_rocprof:
         return summarize_rocprof(args.summarize_rocprof)
+    if args.ragged and args.step != "mixed":
+        print("--ragged needs --step mixed", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the verify step shards by sequence with no exchange; see the design notes).",
@@ -264,6 +269,9 @@ def main() -> int:
     x = torch.from_numpy(case.draft_tokens).to(dev)
     seeds = torch.from_numpy(case.seeds.view(np.int64)).to(dev)
     temps = torch.from_numpy(temps_np.astype(np.float64)).to(dev)
+    klen_np = (np.random.default_rng(54).integers(0, K + 1, size=b).astype(np.int32) if args.ragged
+               else np.full(b, K, np.int32))
+    klen = torch.from_numpy(klen_np).to(dev) if args.ragged else None
     dt = tgt0.dtype
     g0, g1 = (int(gidx[0]), int(gidx[-1]) + 1) if has_g else (0, 0)
     s0, s1 = (int(sidx[0]), int(sidx[-1]) + 1) if has_s else (0, 0)
@@ -287,7 +295,7 @@ def main() -> int:
     def step_mixed(k, evs=None):
         t, d = copies[k % len(copies)]
         L.set_stage_events(evs)
-        L.mixed_accept(t, d, x, temps, seeds, out=out_m, workspace=ws_m, stream=stream)
+        L.mixed_accept(t, d, x, temps, seeds, draft_lengths=klen, out=out_m, workspace=ws_m, stream=stream)
 
     def step_split(k, gev=None, sev=None):
         t, d = copies[k % len(copies)]
@@ -363,11 +371,13 @@ def main() -> int:
         n_s = n_all[sidx] if has_s else np.zeros(0, np.int32)
     else:
         n_s = out_s.n_accepted.cpu().numpy()[:bs] if has_s else np.zeros(0, np.int32)
-    rejected = int(((n_s >= 0) & (n_s < K)).sum())
-    bonus = int((n_s == K).sum())
+    ks = klen_np[sidx] if has_s else np.zeros(0, np.int32)
+    rejected = int(((n_s >= 0) & (n_s < ks)).sum())
+    bonus = int((n_s == ks).sum())
     es = 2 if dt == torch.bfloat16 else 4
-    bytes_greedy = bg * (K + 1) * V * es
-    bytes_sample_pass = bs * (2 * K + 1) * V * es
+    # rows each sequence's block holds: Ks + 1 target rows, plus Ks draft rows when sampled
+    bytes_greedy = int((klen_np[gidx].astype(np.int64) + 1).sum()) * V * es if has_g else 0
+    bytes_sample_pass = int((2 * ks.astype(np.int64) + 1).sum()) * V * es
     # per sampling sequence: one pass over its 2K+1 rows, plus the rejected
     # row pair read again for the residual, or one segment of the bonus row
     bytes_step = bytes_greedy + bytes_sample_pass + rejected * 2 * V * es + bonus * SEG_BYTES
@@ -378,7 +388,8 @@ def main() -> int:
     else:
         dom, dom_bytes, dom_ms = "row_pass", bytes_greedy, stage["greedy_row_pass"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(dom, f"c{args.workload}_{args.step}")
+    wl_key = f"c{args.workload}_{args.step}" + ("_ragged" if args.ragged else "")
+    traffic = load_traffic(dom, wl_key)
 
     result = {
         "metric": "verify blocks/s and achieved HBM GB/s (% of peak), b=128 K=7 V=262144 bf16",
@@ -394,7 +405,9 @@ def main() -> int:
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"c{args.workload}: {W.CONFIG_TEXT[args.workload]}",
+            "workload": f"c{args.workload}: {W.CONFIG_TEXT[args.workload]}" + (
+                "; per-sequence draft lengths uniform on 0..K (seeded)" if args.ragged else ""),
+            "mean_draft_length": float(klen_np.mean()),
             "b": b, "K": K, "V": V, "temperature": case.T,
             "greedy_sequences": bg, "sampling_sequences": bs,
             "step": ("one spec_mixed_accept call (per-sequence temperature 0 / 0.8)" if mixed else

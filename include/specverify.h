@@ -136,7 +136,21 @@ int spec_sample_accept(const void *target, const void *draft, int dtype,
  * spec_greedy_accept / spec_sample_accept give it, with its index s in THIS
  * batch as the Philox row.  Draft rows of greedy sequences are never read.
  *
+ * Each sequence may also carry fewer than K draft tokens: a drafter's
+ * confidence head truncates its block and a draft cap limits it ("mlx-dspark
+ * 0.0.1" sdist diff, README "Tuning" and the --max-draft /
+ * --confidence-threshold flags of its __main__.py; the confidence output of
+ * "dspark-mlx 0.1.0", DraftBackbone.forward_spec).  Sequence s with draft
+ * length Ks = draft_lengths[s], 0 <= Ks <= K, verifies target rows 0..Ks
+ * (row Ks its bonus position), draft rows 0..Ks-1 and draft tokens
+ * 0..Ks-1, exactly as a call with K = Ks would; Ks = 0 commits one token
+ * (the argmax of row 0, or a draw from p_1).  Storage past its block is never
+ * read; outputs past it are -1 (tokens, target_argmax) and NaN (p_draft,
+ * q_draft).  Ks outside [0, K] makes the sequence invalid.  Strides and
+ * output shapes stay those of K.
+ *
  *   temperatures    [b] double (device)
+ *   draft_lengths   [b] int32 (device), or NULL: every sequence has K
  *   p_draft, q_draft  [b, K] float out or NULL (NaN for greedy sequences)
  *   target_argmax   [b, K+1] int32 out or NULL (-1 for sampling sequences)
  *   workspace       spec_mixed_workspace_bytes(b, K, V, dtype) bytes (device)
@@ -149,7 +163,8 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype,
                       int64_t t_batch_stride, int64_t t_row_stride,
                       int64_t d_batch_stride, int64_t d_row_stride,
                       const int32_t *draft_tokens, int b, int K, int V,
-                      const double *temperatures, const uint64_t *seeds,
+                      const double *temperatures, const int32_t *draft_lengths,
+                      const uint64_t *seeds,
                       int32_t *n_accepted, int32_t *tokens,
                       float *p_draft, float *q_draft, int32_t *target_argmax,
                       void *workspace, size_t workspace_bytes, void *hip_stream);

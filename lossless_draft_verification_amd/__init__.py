@@ -62,7 +62,7 @@ def _load():
     lib.spec_sample_accept.restype = i32
     lib.spec_mixed_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_mixed_workspace_bytes.restype = sz
-    lib.spec_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp,
+    lib.spec_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_mixed_accept.restype = i32
     lib.spec_set_stage_events.argtypes = [vp, i32]
@@ -208,11 +208,14 @@ def speculative_sample_accept(target: torch.Tensor, draft: torch.Tensor, draft_t
 
 
 def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
-                 temperatures: torch.Tensor, seeds: torch.Tensor, *, out: Optional[AcceptResult] = None,
+                 temperatures: torch.Tensor, seeds: torch.Tensor, *,
+                 draft_lengths: Optional[torch.Tensor] = None, out: Optional[AcceptResult] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None) -> AcceptResult:
     """Mixed batch: sequence s is greedy when temperatures[s] == 0 and sampled
     at temperatures[s] otherwise (float64 device tensor [b]).  Philox rows are
-    the sequences' indices in this batch."""
+    the sequences' indices in this batch.  draft_lengths (int32 device tensor
+    [b], or None for all K): sequence s verifies only its first
+    draft_lengths[s] draft tokens (0..K; anything else marks it invalid)."""
     _on_gpu(target, draft, draft_tokens, temperatures, seeds)
     if target.dim() != 3 or draft.dim() != 3 or target.stride(2) != 1 or draft.stride(2) != 1:
         raise ValueError("target [b, K+1, V] and draft [b, K, V] need V contiguous")
@@ -226,6 +229,11 @@ def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.
         raise ValueError("temperatures must be a contiguous float64 [b] tensor")
     if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
         raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    if draft_lengths is not None:
+        _on_gpu(draft_lengths)
+        if (draft_lengths.shape != (b,) or draft_lengths.dtype != torch.int32
+                or not draft_lengths.is_contiguous()):
+            raise ValueError("draft_lengths must be a contiguous int32 [b] tensor")
     dev = target.device
     if out is None:
         out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
@@ -238,6 +246,7 @@ def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.
     rc = _lib.spec_mixed_accept(
         target.data_ptr(), draft.data_ptr(), _dtype_code(target), target.stride(0), target.stride(1),
         draft.stride(0), draft.stride(1), draft_tokens.data_ptr(), b, K, V, temperatures.data_ptr(),
+        draft_lengths.data_ptr() if draft_lengths is not None else None,
         seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
         out.p_draft.data_ptr() if out.p_draft is not None else None,
         out.q_draft.data_ptr() if out.q_draft is not None else None,

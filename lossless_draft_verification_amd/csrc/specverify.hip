@@ -285,6 +285,7 @@ struct Ctx {
     int K, V, nseg, nres, rps;         // rps: partial rows per sequence (K+1 or 2K+1)
     const double *temps;               // per-sequence temperatures, or NULL
     double T_uniform;                  // the call's temperature when temps is NULL
+    const int32_t *klen;               // per-sequence draft lengths [b], or NULL (all K)
     const int32_t *x;                  // draft tokens [b, K]
     const uint64_t *seeds;             // [b]
     int32_t *n_out, *tok;              // [b], [b, K+1]
@@ -296,6 +297,19 @@ struct Ctx {
 };
 
 __device__ inline double seq_temperature(const Ctx &c, int s) { return c.temps ? c.temps[s] : c.T_uniform; }
+
+// Draft length Ks of sequence s: its block is target rows 0..Ks (row Ks the
+// bonus position) and draft rows 0..Ks-1.  A length outside [0, K] makes the
+// sequence invalid.
+__device__ inline int seq_len(const Ctx &c, int s) { return c.klen ? c.klen[s] : c.K; }
+
+__device__ inline int seq_rule(const Ctx &c, double T, int Ks) {
+    return (Ks < 0 || Ks > c.K) ? kRuleInvalid : rule_of(T);
+}
+
+// Whether partial row r (target rows 0..K, then draft rows K+1..2K) is part
+// of the block of a sequence with draft length Ks.
+__device__ inline bool row_in_block(int r, int K, int Ks) { return r <= K ? r <= Ks : r - (K + 1) < Ks; }
 
 // ---------------------------------------------------------------------------
 // Row pass, one wave: segment `seg` of row i of sequence s.  Greedy rows keep
@@ -414,7 +428,8 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         if (r < rps && lane < nseg) pre[k] = c.part[((int64_t)s * rps + r) * nseg + lane];
     }
     const double T = seq_temperature(c, s);
-    const int rule = rule_of(T);
+    const int Ks = seq_len(c, s);
+    const int rule = seq_rule(c, T, Ks);
     int32_t *tok = c.tok + (int64_t)s * K1;
 
     if (rule == kRuleInvalid) {
@@ -446,7 +461,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     int32_t x = 0;
     bool tok_bad = false;
     float zt = 0.0f, zd = 0.0f;
-    if (wave == 0 && lane < K) {
+    if (wave == 0 && lane < Ks) {
         x = c.x[(int64_t)s * K + lane];
         tok_bad = x < 0 || x >= V;
         if (rule == kRuleSample && !tok_bad) {
@@ -485,8 +500,8 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         };
 #pragma unroll
         for (int k = 0; k < kPre; ++k)
-            if (wave + k * NW < K1) merge_row(wave + k * NW, &pre[k]);
-        for (int i = wave + kPre * NW; i < K1; i += NW) merge_row(i, nullptr);
+            if (wave + k * NW <= Ks) merge_row(wave + k * NW, &pre[k]);
+        for (int i = wave + kPre * NW; i <= Ks; i += NW) merge_row(i, nullptr);
         __syncthreads();
         if (wave != 0) return;
         const bool invalid = sBad || (__ballot(tok_bad) != 0ull);
@@ -507,12 +522,12 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
             if (lane == 0) c.n_out[s] = -1;
             return;
         }
-        const bool mismatch = lane < K && x != sA[lane];
+        const bool mismatch = lane < Ks && x != sA[lane];
         const unsigned long long mm = __ballot(mismatch);
-        const int n = mm ? (int)__ffsll((long long)mm) - 1 : K;
+        const int n = mm ? (int)__ffsll((long long)mm) - 1 : Ks;
         if (lane < K1) {
             tok[lane] = lane < n ? x : lane == n ? sA[n] : -1;
-            if (c.am) c.am[(int64_t)s * K1 + lane] = sA[lane];
+            if (c.am) c.am[(int64_t)s * K1 + lane] = lane <= Ks ? sA[lane] : -1;
         }
         if (lane == 0) c.n_out[s] = n;
         return;
@@ -551,9 +566,12 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         }
     };
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
-        if (wave + k * NW < R) merge_row(wave + k * NW, &pre[k]);
-    for (int r = wave + kPre * NW; r < R; r += NW) merge_row(r, nullptr);
+    for (int k = 0; k < kPre; ++k) {
+        const int r = wave + k * NW;
+        if (r < R && row_in_block(r, K, Ks)) merge_row(r, &pre[k]);
+    }
+    for (int r = wave + kPre * NW; r < R; r += NW)
+        if (row_in_block(r, K, Ks)) merge_row(r, nullptr);
     __syncthreads();
     if (wave != 0) return;
 
@@ -575,7 +593,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     }
     const uint64_t seed = c.seeds[s];
     bool reject = false;
-    if (lane < K) {
+    if (lane < Ks) {
         const double lp = ((double)zt - (double)sM[lane]) / T - log(sS[lane]);
         const double lq = ((double)zd - (double)sM[K1 + lane]) / T - log(sS[K1 + lane]);
         double r;
@@ -586,14 +604,17 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         reject = !(u < r);                            // u < 1, so u < r == u < min(1, r)
         if (c.p_out) c.p_out[(int64_t)s * K + lane] = (float)exp(lp);
         if (c.q_out) c.q_out[(int64_t)s * K + lane] = (float)exp(lq);
+    } else if (lane < K) {                            // slots past the block
+        if (c.p_out) c.p_out[(int64_t)s * K + lane] = NAN;
+        if (c.q_out) c.q_out[(int64_t)s * K + lane] = NAN;
     }
     const unsigned long long rj = __ballot(reject);
-    const int n = rj ? (int)__ffsll((long long)rj) - 1 : K;
+    const int n = rj ? (int)__ffsll((long long)rj) - 1 : Ks;
     if (lane < K1) tok[lane] = lane < n ? x : -1;     // slot n is filled by the draw
     if (lane == 0) {
         c.n_out[s] = n;
         DrawPlan pl;
-        pl.mode = n < K ? kModeResidual : kModeTarget;
+        pl.mode = n < Ks ? kModeResidual : kModeTarget;
         pl.slot = n;
         pl.u2 = philox_uniform(seed, (uint32_t)s, (uint32_t)n, 1u);
         pl.T = T;
@@ -603,7 +624,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         pl.St = St;
         pl.Lt_hi = (float)Lt;
         pl.Lt_lo = (float)(Lt - (double)pl.Lt_hi);
-        if (n < K) {
+        if (n < Ks) {
             const double Ld = log2(sS[K1 + n]);
             pl.Md = sM[K1 + n];
             pl.Ld_hi = (float)Ld;
@@ -849,7 +870,8 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
 
 // Row pass: one single-wave workgroup per (row of the call, segment), rows
 // taken sequence by sequence, rps per sequence.  Draft rows of greedy
-// sequences and rows of invalid sequences are skipped.  (Single-wave
+// sequences, rows past a sequence's draft length and rows of invalid
+// sequences are skipped.  (Single-wave
 // workgroups stream measurably faster on this part than 4-wave ones: a wave
 // starts as soon as one wave's resources free up.)
 template <int DT, bool VEC>
@@ -859,8 +881,9 @@ __global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
     const int seg = blockIdx.x - row * c.nseg;
     const int s = row / c.rps, i = row - s * c.rps;
     const double T = seq_temperature(c, s);
-    const int rule = rule_of(T);
-    if (rule == kRuleInvalid || (rule == kRuleGreedy && i > c.K)) return;
+    const int Ks = seq_len(c, s);
+    const int rule = seq_rule(c, T, Ks);
+    if (rule == kRuleInvalid || (rule == kRuleGreedy && i > c.K) || !row_in_block(i, c.K, Ks)) return;
     row_wave<DT, VEC>(c, s, i, seg, lane, rule, T);
 }
 
@@ -1076,7 +1099,7 @@ int spec_sample_accept(const void *target, const void *draft, int dtype, int64_t
 int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
                       int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
                       const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
-                      const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, float *p_draft,
+                      const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, float *p_draft,
                       float *q_draft, int32_t *target_argmax, void *workspace, size_t workspace_bytes,
                       void *hip_stream) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
@@ -1098,6 +1121,7 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t 
     c.K = K;
     c.V = V;
     c.temps = temperatures;
+    c.klen = draft_lengths;
     c.x = draft_tokens;
     c.seeds = seeds;
     c.n_out = n_accepted;

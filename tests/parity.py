@@ -100,8 +100,9 @@ def _draw_near_tie(case: W.Case, res: dict, s: int, slot: int, y_g: int, T: floa
 
 
 def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str, res: dict = None,
-                   temps=None) -> Report:
-    """Sampling sequences of `case` (all of them, or those with temps > 0)."""
+                   temps=None, lens=None) -> Report:
+    """Sampling sequences of `case` (all of them, or those with temps > 0);
+    sequence s has lens[s] draft tokens (all K when lens is None)."""
     if res is None:
         res = oracle.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
     if temps is None:
@@ -109,14 +110,16 @@ def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str, res: dict = No
     seqs = [s for s in range(case.b) if temps[s] != 0.0]
     n_o, tok_o = res["n_accepted"], res["tokens"]
     rep = Report(sequences=len(seqs), sampling_sequences=len(seqs))
-    K = case.K
     with np.errstate(invalid="ignore"):
         band = np.abs(res["u"] - np.minimum(1.0, res["r"])) < ACCEPT_BAND
     for s in seqs:
-        # probabilities of every slot
+        K = case.K if lens is None else int(lens[s])
+        # probabilities of every slot of the block; NaN past it
         if n_o[s] >= 0:
+            if not (np.isnan(p_g[s, K:]).all() and np.isnan(q_g[s, K:]).all()):
+                rep.failures.append(dict(case=name, seq=s, what="probabilities past the block"))
             for arr_g, arr_o in ((p_g, res["p_draft"]), (q_g, res["q_draft"])):
-                g, o = arr_g[s].astype(np.float64), arr_o[s]
+                g, o = arr_g[s, :K].astype(np.float64), arr_o[s, :K]
                 ok = np.isclose(g, o, rtol=PROB_RTOL, atol=1e-37)
                 rel = np.abs(g - o) / np.maximum(np.abs(o), 1e-300)
                 rep.max_prob_rel_err = max(rep.max_prob_rel_err, float(rel[o > 1e-30].max(initial=0.0)))
@@ -156,9 +159,10 @@ def compare_sample(case: W.Case, n_g, tok_g, p_g, q_g, name: str, res: dict = No
     return rep
 
 
-def compare_mixed(case: W.Case, temps: np.ndarray, n_g, tok_g, p_g, q_g, am_g, name: str) -> Report:
-    res = oracle.mixed_accept(case.target, case.draft, case.draft_tokens, temps, case.seeds)
-    rep = compare_sample(case, n_g, tok_g, p_g, q_g, name, res=res, temps=temps)
+def compare_mixed(case: W.Case, temps: np.ndarray, n_g, tok_g, p_g, q_g, am_g, name: str,
+                  lens=None) -> Report:
+    res = oracle.mixed_accept(case.target, case.draft, case.draft_tokens, temps, case.seeds, lens)
+    rep = compare_sample(case, n_g, tok_g, p_g, q_g, name, res=res, temps=temps, lens=lens)
     greedy = np.nonzero(temps == 0.0)[0]
     rep.sequences += len(greedy)
     rep.greedy_sequences += len(greedy)
@@ -177,14 +181,16 @@ def compare_mixed(case: W.Case, temps: np.ndarray, n_g, tok_g, p_g, q_g, am_g, n
     return rep
 
 
-def run_gpu_mixed(case: W.Case, temps: np.ndarray, target_dev=None, draft_dev=None):
+def run_gpu_mixed(case: W.Case, temps: np.ndarray, target_dev=None, draft_dev=None, lens=None,
+                  draft_tokens=None):
     import lossless_draft_verification_amd as L
     t = to_device(case.target) if target_dev is None else target_dev
     d = to_device(case.draft) if draft_dev is None else draft_dev
-    x = torch.from_numpy(case.draft_tokens).cuda()
+    x = torch.from_numpy(case.draft_tokens if draft_tokens is None else draft_tokens).cuda()
     sd = seeds_to_device(case.seeds)
     T = torch.from_numpy(np.ascontiguousarray(temps, dtype=np.float64)).cuda()
-    r = L.mixed_accept(t, d, x, T, sd)
+    kl = None if lens is None else torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    r = L.mixed_accept(t, d, x, T, sd, draft_lengths=kl)
     torch.cuda.synchronize()
     return (r.n_accepted.cpu().numpy(), r.tokens.cpu().numpy(), r.p_draft.cpu().numpy(),
             r.q_draft.cpu().numpy(), r.argmax.cpu().numpy())

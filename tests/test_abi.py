@@ -99,6 +99,31 @@ def test_sample_argument_validation(lib):
     assert _sample(lib, draft=18, dtype=0) == 3   # fp32 needs 4-byte alignment
 
 
+def _mixed(lib, **kw):
+    a = dict(target=16, draft=16, dtype=1, tbs=800, trs=100, dbs=700, drs=100, tok=16, b=2, K=7, V=100,
+             temps=16, lens=None, seeds=16, n=16, tokens=16, p=None, q=None, am=None, ws=16, wsb=1 << 20,
+             stream=None)
+    a.update(kw)
+    return lib.spec_mixed_accept(a["target"], a["draft"], a["dtype"], a["tbs"], a["trs"], a["dbs"],
+                                 a["drs"], a["tok"], a["b"], a["K"], a["V"], a["temps"], a["lens"],
+                                 a["seeds"], a["n"], a["tokens"], a["p"], a["q"], a["am"], a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+def test_mixed_argument_validation(lib):
+    assert _mixed(lib, temps=None) == 1
+    assert _mixed(lib, draft=None) == 1
+    assert _mixed(lib, seeds=None) == 1
+    assert _mixed(lib, lens=16, K=0) == 1
+    assert _mixed(lib, lens=16, K=33) == 1
+    assert _mixed(lib, lens=16, trs=99) == 1
+    assert _mixed(lib, lens=16, wsb=64) == 1
+    assert _mixed(lib, dtype=4) == 2
+    assert _mixed(lib, lens=16, target=15) == 3
+    need = lib.spec_mixed_workspace_bytes(2, 7, 100, 1)
+    assert need >= lib.spec_workspace_bytes(2, 7, 100, 1, 1) > 0
+
+
 def test_stream_copy_validation(lib):
     assert lib.spec_stream_copy(None, 16, 16, None) == 1
     assert lib.spec_stream_copy(16, 16, 15, None) == 1

@@ -216,3 +216,61 @@ def test_workload_c5_mixed_call():
     case = W.config(5)
     temps = np.where(case.rule == W.GREEDY, 0.0, case.T)
     _check(compare_mixed(case, temps, *run_gpu_mixed(case, temps), "c5_mixed"), "workload_c5_mixed")
+
+
+# ------------------------------------------------- per-sequence draft lengths
+
+
+def _ragged_case(case: W.Case, lens: np.ndarray) -> tuple:
+    """Poison every byte past each sequence's block (NaN logits, out-of-range
+    draft tokens): neither side may read them."""
+    import dataclasses
+    t, d, x = case.target.copy(), case.draft.copy(), case.draft_tokens.copy()
+    nan = np.uint16(0x7FC0) if t.dtype == np.uint16 else np.float32(np.nan)
+    for s, k in enumerate(lens):
+        k = int(min(max(k, -1), case.K))
+        t[s, k + 1:] = nan
+        d[s, max(k, 0):] = nan
+        x[s, max(k, 0):] = -3
+    return dataclasses.replace(case, target=t, draft=d, draft_tokens=x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_small(dtype):
+    """Draft lengths 0..K (and two out of range) in one mixed batch."""
+    b, K = 40, 6
+    base = W.make_case("ragged", b=b, K=K, V=20011, dtype=dtype, target_scale=2.5,
+                       draft_sigma=(0.2, 1.5), T=0.8, seed=51)
+    rng = np.random.default_rng(52)
+    lens = rng.integers(0, K + 1, size=b).astype(np.int32)
+    lens[:K + 1] = np.arange(K + 1)
+    lens[K + 1:2 * K + 2] = np.arange(K + 1)
+    lens[-1], lens[-2] = -1, K + 1
+    temps = np.where(np.arange(b) % (K + 1) < (K + 1) // 2, 0.0, 0.8)
+    temps[K + 1:2 * K + 2] = 0.8 - 0.8 * (np.arange(K + 1) % 2)
+    case = _ragged_case(base, lens)
+    out = run_gpu_mixed(case, temps, lens=lens)
+    assert out[0][-1] == -1 and out[0][-2] == -1
+    assert (out[0][:-2] >= 0).all() and (out[0][:-2] <= lens[:-2]).all()
+    _check(compare_mixed(case, temps, *out, f"ragged_small_{dtype}", lens=lens), f"ragged_small_{dtype}")
+
+
+def test_ragged_full_lengths_equal_no_lengths():
+    """draft_lengths all K gives the same bits as no draft_lengths."""
+    case = W.make_case("ragK", b=10, K=5, V=30000, dtype="bf16", target_scale=3.0,
+                       draft_sigma=(0.1, 2.0), T=0.8, seed=53)
+    temps = np.array([0.0, 0.8] * 5)
+    a = run_gpu_mixed(case, temps)
+    b_ = run_gpu_mixed(case, temps, lens=np.full(case.b, case.K, np.int32))
+    for u, v in zip(a, b_):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_workload_c5_ragged():
+    """b=128, K=7, V=262144 bf16, mixed rules, draft lengths uniform on 0..7."""
+    base = W.config(5)
+    lens = np.random.default_rng(54).integers(0, base.K + 1, size=base.b).astype(np.int32)
+    case = _ragged_case(base, lens)
+    temps = np.where(case.rule == W.GREEDY, 0.0, case.T)
+    out = run_gpu_mixed(case, temps, lens=lens)
+    _check(compare_mixed(case, temps, *out, "c5_ragged", lens=lens), "workload_c5_ragged")

@@ -246,3 +246,104 @@ def config(cid: int, b: Optional[int] = None, V: Optional[int] = None) -> Case:
                          target_scale=3.0, draft_sigma=(0.1, 2.0), rule=rules, T=0.8,
                          seed=seed, spike_prob=0.01)
     raise ValueError(f"unknown workload {cid}")
+
+
+# ---------------------------------------------------------------------------
+# Fused verify inputs: the verify forward's final hidden states and the
+# lm_head weight instead of a materialised target logit block.
+#
+# The lm_head is a bias-free Linear(hidden_size, vocab_size) followed by the
+# final-logit softcap; hidden_size 3840, vocab_size 262144, softcap 30 are
+# the Gemma-4 drafter arguments ("dspark-mlx 0.1.0" wheel diff,
+# dspark_mlx/arch/gemma4.py).  The drafter's logits arrive in float32 (it
+# applies its lm_head to float32 hidden states, same file).
+#
+# Recipe (no product of hidden and weight is formed here):
+#   hidden      iid N(0, 1), bf16
+#   weight      iid N(0, scale^2 / D), bf16, so background logits ~ N(0, scale^2)
+#   planted     each target row (s, i) gets its own token t[s, i] (distinct
+#               tokens); weight row t[s, i] is set to bf16(g / D * hidden[s, i])
+#               with a gain g ~ U[gain_lo, gain_hi], so that row's logit at
+#               t[s, i] is about g and elsewhere about N(0, scale^2)
+#   draft       float32 [b, K, V]: iid N(0, draft_scale^2) plus, at t[s, i],
+#               0.9 g + N(0, 1) (a drafter that mostly agrees)
+#   tokens      greedy sequences: t[s, i] with probability agree, else another
+#               uniform token; sampling sequences: a draw from softmax(draft / T)
+#               (Gumbel-max)
+#   temps       0 for greedy sequences, T for sampling sequences
+
+
+@dataclass
+class FusedCase:
+    name: str
+    b: int
+    K: int
+    V: int
+    D: int
+    softcap: float
+    T: float
+    hidden: np.ndarray              # [b, K+1, D] uint16 bf16 bits
+    weight: np.ndarray              # [V, D] uint16 bf16 bits
+    draft: np.ndarray               # [b, K, V] float32
+    draft_tokens: np.ndarray        # [b, K] int32
+    seeds: np.ndarray               # [b] uint64
+    temps: np.ndarray               # [b] float64 (0 = greedy)
+    planted: np.ndarray             # [b, K+1] int32
+    meta: dict = field(default_factory=dict)
+
+
+def make_fused_case(name: str, *, b: int, K: int, V: int, D: int, softcap: float = 30.0,
+                    scale: float = 3.0, gain: Tuple[float, float] = (10.0, 24.0),
+                    draft_scale: float = 3.0, agree: float = 0.85,
+                    rule: Union[int, Sequence[int]] = SAMPLING, T: float = 0.8,
+                    seed: int = 0) -> FusedCase:
+    if V < b * (K + 1):
+        raise ValueError("need V >= b*(K+1) for distinct planted tokens")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rules = np.full(b, int(rule), np.int32) if np.isscalar(rule) else np.asarray(rule, np.int32)
+    assert rules.shape == (b,)
+    hidden = bf16_bits(rng.standard_normal((b, K + 1, D), dtype=np.float32))
+    weight = np.empty((V, D), np.uint16)
+    wscale = np.float32(scale / np.sqrt(D))
+    slab = max(1, (1 << 24) // D)
+    for v0 in range(0, V, slab):
+        v1 = min(V, v0 + slab)
+        weight[v0:v1] = bf16_bits(rng.standard_normal((v1 - v0, D), dtype=np.float32) * wscale)
+    planted = rng.choice(V, size=b * (K + 1), replace=False).astype(np.int32).reshape(b, K + 1)
+    g = rng.uniform(gain[0], gain[1], size=(b, K + 1))
+    hf = bf16_to_f32(hidden)
+    for s in range(b):
+        for i in range(K + 1):
+            weight[planted[s, i]] = bf16_bits(hf[s, i] * np.float32(g[s, i] / D))
+    draft = np.empty((b, K, V), np.float32)
+    for s in range(b):
+        draft[s] = rng.standard_normal((K, V), dtype=np.float32) * np.float32(draft_scale)
+        for i in range(K):
+            draft[s, i, planted[s, i]] = np.float32(0.9 * g[s, i] + rng.standard_normal())
+    tokens = np.empty((b, K), np.int32)
+    for s in range(b):
+        for i in range(K):
+            if rules[s] == GREEDY:
+                if rng.random() < agree:
+                    tokens[s, i] = planted[s, i]
+                else:
+                    tokens[s, i] = (planted[s, i] + 1 + int(rng.integers(V - 1))) % V
+            else:
+                tokens[s, i] = _gumbel_draw(rng, draft[s, i], T)
+    temps = np.where(rules == GREEDY, 0.0, float(T))
+    meta = {"seed": seed, "gain": g, "scale": scale}
+    return FusedCase(name, b, K, V, D, float(softcap), float(T), hidden, weight, draft, tokens,
+                     np.arange(b, dtype=np.uint64), temps, planted, meta)
+
+
+FUSED_TEXT = ("b=128 K=7 V=262144 D=3840: bf16 hidden states [b, K+1, D] N(0,1) and bf16 lm_head "
+              "weight [V, D] N(0, 3^2/D) with one planted token per target row (gain ~ U[10,24]), "
+              "final-logit softcap 30, fp32 drafter logits, rows 0..63 greedy / 64..127 sampling "
+              "T=0.8")
+
+
+def fused_config(b: int = 128, K: int = 7, V: int = 262144, D: int = 3840) -> FusedCase:
+    """The fused verify workload at the 262144-entry Gemma-4 vocabulary (data
+    seed 6001); smaller b / V / D keep the recipe."""
+    rules = np.array([GREEDY] * (b // 2) + [SAMPLING] * (b - b // 2), np.int32)
+    return make_fused_case("fused", b=b, K=K, V=V, D=D, softcap=30.0, rule=rules, T=0.8, seed=6001)

@@ -170,12 +170,70 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype,
                       void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * Fused verify: the target logit block is formed inside the call from the
+ * verify forward's final hidden states and the lm_head weight, and never
+ * stored for greedy sequences.  The logits are those of the Gemma-4 drafter
+ * code ("dspark-mlx 0.1.0" wheel diff, dspark_mlx/arch/gemma4.py): a
+ * bias-free Linear(hidden_size, vocab_size) with weight [V, D] applied to
+ * float32 hidden states, then the final-logit softcap c*tanh(a/c):
+ *
+ *   z[s, i, v] = softcap( sum_d hidden[s, i, d] * weight[v, d] ),  i = 0..K
+ *
+ * computed on the matrix cores from bf16 operands (products exact, sums in
+ * float32, any order: within gamma_D * sum_d |hidden * weight| of the exact
+ * sum, gamma_D = D 2^-24 / (1 - D 2^-24)); the softcap adds at most
+ * 4 * 2^-23 * c.  Everything after the logits is spec_mixed_accept's
+ * (per-sequence temperature, optional draft lengths), on float32 logits.
+ *
+ *   hidden        bf16 [b, K+1, D] (device), element strides h_batch_stride,
+ *                 h_row_stride (multiples of 8), 16-byte aligned; it must span
+ *                 fewer than 2^31 elements
+ *   weight        bf16 [V, D] (device), row stride w_row_stride (a multiple of
+ *                 8, >= D), 16-byte aligned
+ *   D             a positive multiple of 64
+ *   softcap       c >= 0 (0 = no softcap)
+ *   draft         float32 [b, K, V] drafter logits (device), element strides
+ *   workspace     spec_fused_workspace_bytes(b, K, V, D) bytes, 256-byte
+ *                 aligned.  It holds, besides the partials, the float32 logits
+ *                 of the sampling sequences (their residual or bonus draw
+ *                 re-reads one row), b*(K+1)*ceil64(V)*4 bytes.
+ * Other arguments and outputs as for spec_mixed_accept.  Seven kernels:
+ * lm_head GEMM with statistics epilogue, tile merge, draft-row pass, scan,
+ * residual pass, draw.  Errors as for spec_mixed_accept; misaligned
+ * operands give SPEC_EALIGN.
+ */
+size_t spec_fused_workspace_bytes(int b, int K, int V, int D);
+
+int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t h_row_stride,
+                            const void *weight, int64_t w_row_stride, int D, float softcap,
+                            const float *draft, int64_t d_batch_stride, int64_t d_row_stride,
+                            const int32_t *draft_tokens, int b, int K, int V,
+                            const double *temperatures, const int32_t *draft_lengths,
+                            const uint64_t *seeds,
+                            int32_t *n_accepted, int32_t *tokens,
+                            float *p_draft, float *q_draft, int32_t *target_argmax,
+                            void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * The fused call's GEMM alone: logits[r, v] = softcap(sum_d hidden[r, d] *
+ * weight[v, d]) in float32 for rows r < rows, written with row stride
+ * l_row_stride (a multiple of 4, >= V; logits 16-byte aligned).  Same
+ * kernel, same arithmetic, as inside spec_fused_mixed_accept; for checking
+ * the logits and for callers that want them.  hidden: bf16 [rows, D], row
+ * stride h_row_stride.  Same argument rules otherwise.
+ */
+int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows,
+                        const void *weight, int64_t w_row_stride, int V, int D, float softcap,
+                        float *logits, int64_t l_row_stride, void *hip_stream);
+
+/*
  * Profiling hook (not part of the accept semantics).  Registers, for the
  * calling host thread only, an array of n_events hipEvent_t handles.  While
  * registered, each accept call records events[0] before its first kernel and
  * events[k] after its k-th kernel on its stream (kernels: 1 row pass, 2 scan,
- * then for sampling and mixed calls 3 residual pass, 4 draw), for every
- * k < n_events; n_events = 2 brackets the row pass alone.  Pass NULL / 0 to
+ * then for sampling and mixed calls 3 residual pass, 4 draw; for the fused
+ * call 1 lm_head GEMM, 2 tile merge, 3 draft-row pass, 4 scan, 5 residual,
+ * 6 draw), for every k < n_events; n_events = 2 brackets the first kernel.  Pass NULL / 0 to
  * unregister.  Returns SPEC_OK.
  */
 int spec_set_stage_events(void *const *events, int n_events);

@@ -24,6 +24,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_accept",
+           "fused_mixed_accept", "lm_head_logits", "fused_workspace_bytes",
            "workspace_bytes", "mixed_workspace_bytes",
            "set_stage_events", "stream_copy", "library_path", "SpecError"]
 
@@ -65,6 +66,14 @@ def _load():
     lib.spec_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_mixed_accept.restype = i32
+    f32 = ctypes.c_float
+    lib.spec_fused_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_fused_workspace_bytes.restype = sz
+    lib.spec_fused_mixed_accept.argtypes = [vp, i64, i64, vp, i64, i32, f32, vp, i64, i64, vp, i32, i32,
+                                            i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_fused_mixed_accept.restype = i32
+    lib.spec_lm_head_logits.argtypes = [vp, i64, i32, vp, i64, i32, i32, f32, vp, i64, vp]
+    lib.spec_lm_head_logits.restype = i32
     lib.spec_set_stage_events.argtypes = [vp, i32]
     lib.spec_set_stage_events.restype = i32
     lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
@@ -252,6 +261,88 @@ def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.
         out.q_draft.data_ptr() if out.q_draft is not None else None,
         out.argmax.data_ptr() if out.argmax is not None else None,
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+def fused_workspace_bytes(b: int, K: int, V: int, D: int) -> int:
+    n = _lib.spec_fused_workspace_bytes(b, K, V, D)
+    if n == 0:
+        raise ValueError(f"sizes out of range: b={b} K={K} V={V} D={D} (D a multiple of 64)")
+    return n
+
+
+def fused_mixed_accept(hidden: torch.Tensor, weight: torch.Tensor, draft: torch.Tensor,
+                       draft_tokens: torch.Tensor, temperatures: torch.Tensor, seeds: torch.Tensor, *,
+                       softcap: float = 0.0, draft_lengths: Optional[torch.Tensor] = None,
+                       out: Optional[AcceptResult] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> AcceptResult:
+    """Fused verify: target logits softcap(hidden @ weight.T) formed inside
+    the call (bf16 hidden [b, K+1, D], bf16 weight [V, D]), then the mixed
+    accept of mixed_accept with float32 drafter logits draft [b, K, V]."""
+    _on_gpu(hidden, weight, draft, draft_tokens, temperatures, seeds)
+    if hidden.dim() != 3 or hidden.dtype != torch.bfloat16 or hidden.stride(2) != 1:
+        raise ValueError("hidden must be bf16 [b, K+1, D] with D contiguous")
+    if weight.dim() != 2 or weight.dtype != torch.bfloat16 or weight.stride(1) != 1:
+        raise ValueError("weight must be bf16 [V, D] with D contiguous")
+    b, K1, D = hidden.shape
+    K = K1 - 1
+    V = weight.shape[0]
+    if weight.shape[1] != D:
+        raise ValueError("hidden and weight disagree on D")
+    if draft.shape != (b, K, V) or draft.dtype != torch.float32 or draft.stride(2) != 1:
+        raise ValueError("draft must be float32 [b, K, V] with V contiguous")
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    if temperatures.shape != (b,) or temperatures.dtype != torch.float64 or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be a contiguous float64 [b] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    if draft_lengths is not None:
+        _on_gpu(draft_lengths)
+        if (draft_lengths.shape != (b,) or draft_lengths.dtype != torch.int32
+                or not draft_lengths.is_contiguous()):
+            raise ValueError("draft_lengths must be a contiguous int32 [b] tensor")
+    dev = hidden.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           p_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           q_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           argmax=torch.empty(b, K1, dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, fused_workspace_bytes(b, K, V, D), dev)
+    rc = _lib.spec_fused_mixed_accept(
+        hidden.data_ptr(), hidden.stride(0), hidden.stride(1), weight.data_ptr(), weight.stride(0), D,
+        float(softcap), draft.data_ptr(), draft.stride(0), draft.stride(1), draft_tokens.data_ptr(), b, K, V,
+        temperatures.data_ptr(), draft_lengths.data_ptr() if draft_lengths is not None else None,
+        seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.p_draft.data_ptr() if out.p_draft is not None else None,
+        out.q_draft.data_ptr() if out.q_draft is not None else None,
+        out.argmax.data_ptr() if out.argmax is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+def lm_head_logits(hidden: torch.Tensor, weight: torch.Tensor, *, softcap: float = 0.0,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """float32 logits softcap(hidden @ weight.T) for bf16 hidden [rows, D] and
+    weight [V, D]: the fused call's GEMM on its own.  Returns [rows, V] (a
+    view of a buffer whose row stride is V rounded up to 4)."""
+    _on_gpu(hidden, weight)
+    if hidden.dim() != 2 or hidden.dtype != torch.bfloat16 or hidden.stride(1) != 1:
+        raise ValueError("hidden must be bf16 [rows, D] with D contiguous")
+    if weight.dim() != 2 or weight.dtype != torch.bfloat16 or weight.stride(1) != 1:
+        raise ValueError("weight must be bf16 [V, D] with D contiguous")
+    rows, D = hidden.shape
+    V = weight.shape[0]
+    if out is None:
+        out = torch.empty(rows, (V + 3) // 4 * 4, dtype=torch.float32, device=hidden.device)[:, :V]
+    if out.shape != (rows, V) or out.dtype != torch.float32 or out.stride(1) != 1:
+        raise ValueError("out must be float32 [rows, V] with V contiguous")
+    rc = _lib.spec_lm_head_logits(hidden.data_ptr(), hidden.stride(0), rows, weight.data_ptr(), weight.stride(0),
+                                  V, D, float(softcap), out.data_ptr(), out.stride(0),
+                                  _stream_handle(hidden.device, stream))
     _check(rc)
     return out
 

@@ -286,6 +286,7 @@ struct Ctx {
     const double *temps;               // per-sequence temperatures, or NULL
     double T_uniform;                  // the call's temperature when temps is NULL
     const int32_t *klen;               // per-sequence draft lengths [b], or NULL (all K)
+    int row_lo, rpl;                   // row pass: partial rows row_lo .. row_lo+rpl-1 of each sequence
     const int32_t *x;                  // draft tokens [b, K]
     const uint64_t *seeds;             // [b]
     int32_t *n_out, *tok;              // [b], [b, K+1]
@@ -879,7 +880,7 @@ __global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
     const int lane = threadIdx.x;
     const int row = blockIdx.x / c.nseg;
     const int seg = blockIdx.x - row * c.nseg;
-    const int s = row / c.rps, i = row - s * c.rps;
+    const int s = row / c.rpl, i = c.row_lo + (row - s * c.rpl);
     const double T = seq_temperature(c, s);
     const int Ks = seq_len(c, s);
     const int rule = seq_rule(c, T, Ks);
@@ -965,9 +966,11 @@ bool rows_vector_aligned(const void *p, int es, int64_t bs, int64_t rs) {
     return ((uintptr_t)p % 16 == 0) && ((bs * es) % 16 == 0) && ((rs * es) % 16 == 0);
 }
 
+#include "lm_head_fused.inc"
+
 template <int DT, bool VEC>
 int launch(const Ctx &c, int b, int kind, const Layout &L, hipStream_t st) {
-    const int64_t grid_rows = (int64_t)b * L.rps * L.nseg;
+    const int64_t grid_rows = (int64_t)b * c.rpl * L.nseg;
     const int64_t grid_res = (int64_t)b * L.nres;
     if (grid_rows > INT_MAX || grid_res > INT_MAX) return SPEC_EINVAL;
     stage_mark(0, st);
@@ -993,6 +996,8 @@ int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L
     c.nseg = L.nseg;
     c.nres = L.nres;
     c.rps = L.rps;
+    c.row_lo = 0;
+    c.rpl = L.rps;
     c.part = (Partial *)(ws + L.part_off);
     const bool draws = kind != kCallGreedy;
     c.plan = draws ? (DrawPlan *)(ws + L.plan_off) : nullptr;
@@ -1003,6 +1008,68 @@ int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L
     if (dtype == SPEC_BF16)
         return vec ? launch<SPEC_BF16, true>(c, b, kind, L, st) : launch<SPEC_BF16, false>(c, b, kind, L, st);
     return vec ? launch<SPEC_F32, true>(c, b, kind, L, st) : launch<SPEC_F32, false>(c, b, kind, L, st);
+}
+
+// ---------------------------------------------------------------------------
+// Fused verify: workspace layout and launch sequence.
+
+struct FusedLayout {
+    Layout L;                 // the fp32 mixed-call layout (partials, plans, residual masses)
+    int ntiles, tiles_h;
+    int64_t lrs;              // logits row stride (elements, a multiple of 64)
+    size_t tpart_off, logits_off, total;
+};
+
+bool make_fused_layout(int b, int K, int V, int D, FusedLayout &F) {
+    if (D < kLmBK || D % kLmBK != 0) return false;
+    if (!make_layout(b, K, V, SPEC_F32, kCallMixed, F.L)) return false;
+    const int64_t M = (int64_t)b * (K + 1);
+    F.ntiles = (int)(((int64_t)V + kLmBV - 1) / kLmBV);
+    const int64_t th = (M + kLmBH - 1) / kLmBH;
+    if (th > INT_MAX || (int64_t)F.ntiles * th > INT_MAX) return false;
+    F.tiles_h = (int)th;
+    F.lrs = ((int64_t)V + 63) / 64 * 64;
+    F.tpart_off = F.L.total;
+    F.logits_off = F.tpart_off + align256((size_t)M * (size_t)F.ntiles * sizeof(Partial));
+    F.total = F.logits_off + align256((size_t)M * (size_t)F.lrs * sizeof(float));
+    return true;
+}
+
+template <bool VEC>
+int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream_t st) {
+    const Layout &L = F.L;
+    stage_mark(0, st);
+    hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(F.ntiles * F.tiles_h)), dim3(kLmThreads), 0, st, la);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(1, st);
+    const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg;
+    hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c,
+                       (const Partial *)la.tpart, F.ntiles, c.K + 1, b);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(2, st);
+    // draft rows only (partial rows K+1 .. 2K)
+    c.row_lo = c.K + 1;
+    c.rpl = c.K;
+    const int64_t grid_draft = (int64_t)b * c.K * L.nseg;
+    const int64_t grid_res = (int64_t)b * L.nres;
+    if (grid_draft > INT_MAX || grid_res > INT_MAX) return SPEC_EINVAL;
+    hipLaunchKernelGGL((row_pass<SPEC_F32, VEC>), dim3((unsigned)grid_draft), dim3(kWave), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(3, st);
+    hipLaunchKernelGGL((scan_kernel<SPEC_F32>), dim3((unsigned)b), dim3(kScanBlock), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(4, st);
+    hipLaunchKernelGGL((residual_kernel<SPEC_F32, VEC>), dim3((unsigned)grid_res), dim3(kWave), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(5, st);
+    hipLaunchKernelGGL((draw_kernel<SPEC_F32, VEC>), dim3((unsigned)b), dim3(kBlock), 0, st, c);
+    if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    stage_mark(6, st);
+    return SPEC_OK;
+}
+
+bool bf16_operand_ok(const void *p, int64_t stride, int D) {
+    return p && (uintptr_t)p % 16 == 0 && stride >= D && stride % 8 == 0;
 }
 
 }  // namespace
@@ -1141,6 +1208,125 @@ int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream
     if (grid > INT_MAX) return SPEC_EINVAL;
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)grid), dim3(kBlock), 0, (hipStream_t)hip_stream,
                        (uint4 *)dst, (const uint4 *)src, nvec);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+size_t spec_fused_workspace_bytes(int b, int K, int V, int D) {
+    FusedLayout F;
+    if (!make_fused_layout(b, K, V, D, F)) return 0;
+    return F.total;
+}
+
+int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t h_row_stride, const void *weight,
+                            int64_t w_row_stride, int D, float softcap, const float *draft, int64_t d_batch_stride,
+                            int64_t d_row_stride, const int32_t *draft_tokens, int b, int K, int V,
+                            const double *temperatures, const int32_t *draft_lengths, const uint64_t *seeds,
+                            int32_t *n_accepted, int32_t *tokens, float *p_draft, float *q_draft,
+                            int32_t *target_argmax, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    FusedLayout F;
+    if (!make_fused_layout(b, K, V, D, F)) return SPEC_EINVAL;
+    if (!draft || !draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace)
+        return SPEC_EINVAL;
+    if (!hidden || !weight) return SPEC_EINVAL;
+    if (!(softcap >= 0.0f) || !(softcap < INFINITY)) return SPEC_EINVAL;
+    if (d_row_stride < V || d_batch_stride < 0 || h_batch_stride < 0) return SPEC_EINVAL;
+    if (workspace_bytes < F.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
+    if (!bf16_operand_ok(hidden, h_row_stride, D) || !bf16_operand_ok(weight, w_row_stride, D) ||
+        h_batch_stride % 8 != 0)
+        return SPEC_EALIGN;
+    if ((uintptr_t)draft % 4 != 0) return SPEC_EALIGN;
+    // the GEMM keeps 32-bit element offsets into hidden
+    if ((int64_t)(b - 1) * h_batch_stride + (int64_t)K * h_row_stride + D > (int64_t)INT_MAX) return SPEC_EINVAL;
+    char *ws = (char *)workspace;
+    float *logits = (float *)(ws + F.logits_off);
+    LmArgs la = {};
+    la.hidden = (const uint16_t *)hidden;
+    la.hbs = h_batch_stride;
+    la.hrs = h_row_stride;
+    la.weight = (const uint16_t *)weight;
+    la.wrs = w_row_stride;
+    la.b = b;
+    la.K1 = K + 1;
+    la.V = V;
+    la.D = D;
+    la.M = b * (K + 1);
+    la.cap = softcap;
+    la.inv_cap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
+    la.temps = temperatures;
+    la.klen = draft_lengths;
+    la.K = K;
+    la.logits = logits;
+    la.lrs = F.lrs;
+    la.lbs = (int64_t)(K + 1) * F.lrs;
+    la.tpart = (Partial *)(ws + F.tpart_off);
+    la.ntiles = F.ntiles;
+    la.tiles_h = F.tiles_h;
+    la.write_all = 0;
+    Ctx c = {};
+    c.target = logits;
+    c.draft = draft;
+    c.tbs = la.lbs;
+    c.trs = la.lrs;
+    c.dbs = d_batch_stride;
+    c.drs = d_row_stride;
+    c.K = K;
+    c.V = V;
+    c.temps = temperatures;
+    c.klen = draft_lengths;
+    c.x = draft_tokens;
+    c.seeds = seeds;
+    c.n_out = n_accepted;
+    c.tok = tokens;
+    c.p_out = p_draft;
+    c.q_out = q_draft;
+    c.am = target_argmax;
+    const Layout &L = F.L;
+    c.nseg = L.nseg;
+    c.nres = L.nres;
+    c.rps = L.rps;
+    c.row_lo = 0;
+    c.rpl = L.rps;
+    c.part = (Partial *)(ws + L.part_off);
+    c.plan = (DrawPlan *)(ws + L.plan_off);
+    c.rmass = (double *)(ws + L.rmass_off);
+    const bool vec = rows_vector_aligned(draft, 4, d_batch_stride, d_row_stride);
+    return vec ? launch_fused<true>(c, la, b, F, (hipStream_t)hip_stream)
+               : launch_fused<false>(c, la, b, F, (hipStream_t)hip_stream);
+}
+
+int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, const void *weight,
+                        int64_t w_row_stride, int V, int D, float softcap, float *logits, int64_t l_row_stride,
+                        void *hip_stream) {
+    if (rows < 1 || V < 1 || V > INT_MAX - 65536 || D < kLmBK || D % kLmBK != 0) return SPEC_EINVAL;
+    if (!hidden || !weight || !logits) return SPEC_EINVAL;
+    if (!(softcap >= 0.0f) || !(softcap < INFINITY)) return SPEC_EINVAL;
+    if (l_row_stride < V) return SPEC_EINVAL;
+    if (!bf16_operand_ok(hidden, h_row_stride, D) || !bf16_operand_ok(weight, w_row_stride, D)) return SPEC_EALIGN;
+    if ((uintptr_t)logits % 16 != 0 || l_row_stride % 4 != 0) return SPEC_EALIGN;
+    if ((int64_t)(rows - 1) * h_row_stride + D > (int64_t)INT_MAX) return SPEC_EINVAL;
+    const int64_t ntiles = ((int64_t)V + kLmBV - 1) / kLmBV;
+    const int64_t th = ((int64_t)rows + kLmBH - 1) / kLmBH;
+    if (ntiles * th > INT_MAX) return SPEC_EINVAL;
+    LmArgs la = {};
+    la.hidden = (const uint16_t *)hidden;
+    la.hbs = h_row_stride;
+    la.hrs = 0;
+    la.weight = (const uint16_t *)weight;
+    la.wrs = w_row_stride;
+    la.b = rows;
+    la.K1 = 1;
+    la.V = V;
+    la.D = D;
+    la.M = rows;
+    la.cap = softcap;
+    la.inv_cap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
+    la.logits = logits;
+    la.lbs = l_row_stride;
+    la.lrs = 0;
+    la.ntiles = (int)ntiles;
+    la.tiles_h = (int)th;
+    la.write_all = 1;
+    hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(ntiles * th)), dim3(kLmThreads), 0, (hipStream_t)hip_stream, la);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 

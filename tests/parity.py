@@ -215,3 +215,126 @@ def run_gpu_sample(case: W.Case, target_dev=None, draft_dev=None):
     torch.cuda.synchronize()
     return (r.n_accepted.cpu().numpy(), r.tokens.cpu().numpy(), r.p_draft.cpu().numpy(),
             r.q_draft.cpu().numpy())
+
+
+# ------------------------------------------------------------- fused verify
+#
+# The fused path forms its float32 logits in its own summation order, so they
+# differ from the oracle's (the float64 definition rounded once) by at most
+# the float32 summation bound plus the softcap's evaluation error:
+#     tol(v) = gamma_{D+1} * sum_d |h_d w_vd| + 4 * 2^-23 * c + 2^-23 * |z(v)|
+# (gamma_n = n 2^-24 / (1 - n 2^-24); the last term is the rounding of the
+# result).  A decision may then differ from the oracle's only where the
+# oracle sits within that perturbation of the decision boundary:
+#   argmax       z(v_gpu) + tol(v_gpu) >= z(v_oracle) - tol(v_oracle);
+#   accept test  |u - min(1, r)| <= min(1, r) * expm1(delta) + 1e-6,
+#                delta = (tol(x) + max_v tol(v)) / T;
+#   drawn token  t within 2 * expm1(2 max_v tol(v) / T) + 1e-6 R of a CDF
+#                step between the two answers.
+# Probabilities p(x) must agree to expm1(delta) + 1e-5 relative, q(x) to 1e-5.
+
+
+def fused_tolerance(hidden, weight, cap, z64, seqs) -> np.ndarray:
+    import oracle.fused as F
+    D = hidden.shape[-1]
+    tol = F.gamma(D + 1) * F.abs_products(hidden, weight, seqs)
+    tol += 4.0 * 2.0 ** -23 * cap + 2.0 ** -23 * np.abs(z64)
+    return tol
+
+
+def _cdf_near_tie(F, t, R, y_g, y_o, band_abs) -> bool:
+    if y_g < 0 or y_g >= len(F):
+        return False
+    margin = (F[y_g - 1] - t) if y_g > y_o else (t - F[y_g])
+    return margin <= band_abs + 1e-6 * R
+
+
+def compare_fused(case, res_o: dict, tol: np.ndarray, n_g, tok_g, p_g, q_g, am_g, name: str,
+                  lens=None) -> Report:
+    """GPU fused results against the oracle's on the sequences the oracle
+    formed (res_o['seqs']); tol[j] is fused_tolerance for seqs[j]."""
+    seqs = list(res_o["seqs"])
+    rep = Report()
+    n_o, tok_o, am_o = res_o["n_accepted"], res_o["tokens"], res_o["argmax"]
+    K = case.K
+    for j, s in enumerate(seqs):
+        T = float(case.temps[s])
+        Ks = K if lens is None else int(lens[s])
+        z, tl = res_o["logits64"][j], tol[j]
+        rep.sequences += 1
+        if n_o[s] < 0:
+            if n_g[s] == -1 and (tok_g[s] == -1).all():
+                rep.exact_sequences += 1
+            else:
+                rep.failures.append(dict(case=name, seq=s, what="invalid sequence", n_gpu=int(n_g[s])))
+            continue
+        if T == 0.0:
+            rep.greedy_sequences += 1
+            diff = np.nonzero(am_g[s, :Ks + 1] != am_o[s, :Ks + 1])[0]
+            if len(diff) == 0:
+                if n_g[s] == n_o[s] and (tok_g[s] == tok_o[s]).all() and (am_g[s] == am_o[s]).all():
+                    rep.exact_sequences += 1
+                else:
+                    rep.failures.append(dict(case=name, seq=s, what="greedy tokens", n_gpu=int(n_g[s]),
+                                             n_oracle=int(n_o[s])))
+                continue
+            i = int(diff[0])
+            vg, vo = int(am_g[s, i]), int(am_o[s, i])
+            ok = 0 <= vg < case.V and z[i, vg] + tl[i, vg] >= z[i, vo] - tl[i, vo]
+            m = min(i, int(n_g[s]), int(n_o[s]))
+            if ok and (tok_g[s, :m] == tok_o[s, :m]).all():
+                rep.accept_near_tie_mismatch += 1
+            else:
+                rep.failures.append(dict(case=name, seq=s, what="greedy argmax", row=i, gpu=vg, oracle=vo,
+                                         z_gpu_choice=float(z[i, vg]), z_max=float(z[i, vo])))
+            continue
+        rep.sampling_sequences += 1
+        tmax = tl.max(axis=1)
+        x = case.draft_tokens[s]
+        ok_prob = True
+        for i in range(Ks):
+            d = (tl[i, x[i]] + tmax[i]) / T
+            po, qo = res_o["p_draft"][s, i], res_o["q_draft"][s, i]
+            if not abs(p_g[s, i] - po) <= po * (np.expm1(d) + 1e-5) + 1e-37:
+                ok_prob = False
+            if not abs(q_g[s, i] - qo) <= qo * PROB_RTOL + 1e-37:
+                ok_prob = False
+        if not ok_prob:
+            rep.failures.append(dict(case=name, seq=s, what="probabilities", p_gpu=p_g[s].tolist(),
+                                     p_oracle=res_o["p_draft"][s].tolist()))
+            continue
+        if n_g[s] != n_o[s]:
+            i = int(min(n_g[s], n_o[s]))
+            if 0 <= i < Ks:
+                d = (tl[i, x[i]] + tmax[i]) / T
+                u, r = res_o["u"][s, i], min(1.0, res_o["r"][s, i])
+                if abs(u - r) <= r * np.expm1(d) + 1e-6 and (tok_g[s, :i] == tok_o[s, :i]).all():
+                    rep.accept_near_tie_mismatch += 1
+                    continue
+            rep.failures.append(dict(case=name, seq=s, what="accepted length", n_gpu=int(n_g[s]),
+                                     n_oracle=int(n_o[s])))
+            continue
+        n = int(n_o[s])
+        rep.draws += 1
+        if n < Ks:
+            rep.residual_draws += 1
+        else:
+            rep.bonus_draws += 1
+        if (tok_g[s] == tok_o[s]).all():
+            rep.exact_sequences += 1
+            continue
+        if not ((tok_g[s, :n] == tok_o[s, :n]).all() and (tok_g[s, n + 1:] == -1).all()):
+            rep.failures.append(dict(case=name, seq=s, what="tokens", tok_gpu=tok_g[s].tolist(),
+                                     tok_oracle=tok_o[s].tolist()))
+            continue
+        resid = bool(res_o["residual"][s])
+        t1 = np.ascontiguousarray(res_o["logits32"][j:j + 1])
+        d1 = np.ascontiguousarray(case.draft[s:s + 1])
+        F = oracle.draw_cdf(t1, d1, T, 0, n, resid)
+        band = 2.0 * np.expm1(2.0 * tmax[n] / T)
+        if _cdf_near_tie(F, res_o["t"][s], res_o["R"][s], int(tok_g[s, n]), int(tok_o[s, n]), band):
+            rep.draw_near_tie_mismatch += 1
+        else:
+            rep.failures.append(dict(case=name, seq=s, what="drawn token", gpu=int(tok_g[s, n]),
+                                     oracle=int(tok_o[s, n])))
+    return rep

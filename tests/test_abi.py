@@ -124,6 +124,46 @@ def test_mixed_argument_validation(lib):
     assert need >= lib.spec_workspace_bytes(2, 7, 100, 1, 1) > 0
 
 
+def _fused(lib, **kw):
+    a = dict(h=256, hbs=8 * 128, hrs=128, w=512, wrs=128, D=128, cap=30.0, draft=1024, dbs=7 * 1000,
+             drs=1000, tok=16, b=2, K=7, V=1000, temps=16, lens=None, seeds=16, n=16, tokens=16, p=None,
+             q=None, am=None, ws=4096, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_fused_mixed_accept(a["h"], a["hbs"], a["hrs"], a["w"], a["wrs"], a["D"], a["cap"], a["draft"],
+                                       a["dbs"], a["drs"], a["tok"], a["b"], a["K"], a["V"], a["temps"], a["lens"],
+                                       a["seeds"], a["n"], a["tokens"], a["p"], a["q"], a["am"], a["ws"],
+                                       a["wsb"], a["stream"])
+
+
+def test_fused_argument_validation(lib):
+    assert lib.spec_fused_workspace_bytes(2, 7, 1000, 100) == 0          # D not a multiple of 64
+    assert lib.spec_fused_workspace_bytes(2, 7, 1000, 0) == 0
+    need = lib.spec_fused_workspace_bytes(2, 7, 1000, 128)
+    # fp32 mixed layout + tile records + fp32 logits of every row
+    assert need >= lib.spec_mixed_workspace_bytes(2, 7, 1000, 0) + 2 * 8 * 1024 * 4
+    assert _fused(lib, D=96) == 1
+    assert _fused(lib, h=None) == 1
+    assert _fused(lib, w=None) == 1
+    assert _fused(lib, temps=None) == 1
+    assert _fused(lib, cap=-1.0) == 1
+    assert _fused(lib, cap=float("nan")) == 1
+    assert _fused(lib, wsb=1024) == 1
+    assert _fused(lib, ws=4096 + 16) == 1          # workspace not 256-byte aligned
+    assert _fused(lib, h=264) == 3                 # hidden not 16-byte aligned
+    assert _fused(lib, hrs=132) == 3               # row stride not a multiple of 8
+    assert _fused(lib, wrs=120) == 3               # row stride below D
+    assert _fused(lib, draft=1026) == 3
+
+
+def test_lm_head_logits_validation(lib):
+    f = lib.spec_lm_head_logits
+    assert f(256, 128, 0, 512, 128, 1000, 128, 0.0, 1024, 1000, None) == 1
+    assert f(256, 128, 4, 512, 128, 1000, 100, 0.0, 1024, 1000, None) == 1
+    assert f(256, 128, 4, 512, 128, 1000, 128, 0.0, 1024, 999, None) == 1
+    assert f(256, 128, 4, 512, 128, 1000, 128, 0.0, 1028, 1000, None) == 3
+    assert f(256, 128, 4, 512, 128, 1000, 128, 0.0, 1024, 1002, None) == 3
+
+
 def test_stream_copy_validation(lib):
     assert lib.spec_stream_copy(None, 16, 16, None) == 1
     assert lib.spec_stream_copy(16, 16, 15, None) == 1

@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 SEG_BYTES = 16384          # one row-pass segment (the bonus draw re-reads one)
 
 
@@ -204,6 +205,192 @@ def copy_calibration(nbytes: int) -> int:
     return 0
 
 
+def cpu_baseline_fused(case, budget_s: float):
+    """Time the fused-verify oracle (numpy float64 lm_head GEMM + the C
+    accept) on pairs of sequences (one greedy, one sampling) of the workload
+    until the budget is spent."""
+    import numpy as np
+    import oracle.fused as OF
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    g_idx = np.nonzero(case.temps == 0.0)[0]
+    s_idx = np.nonzero(case.temps > 0.0)[0]
+    spent, blocks, k = 0.0, 0, 0
+    while k == 0 or (spent < budget_s and k < min(len(g_idx), len(s_idx))):
+        idx = [int(g_idx[k]), int(s_idx[k])]
+        t0 = time.perf_counter()
+        OF.fused_mixed_accept(case.hidden[idx], case.weight, case.softcap, case.draft[idx],
+                              case.draft_tokens[idx], case.temps[idx], case.seeds[idx])
+        spent += time.perf_counter() - t0
+        blocks += 2
+        k += 1
+    return {
+        "value": blocks / spent, "unit": "verify blocks/s", "cores": cores, "kind": "oracle",
+        "sample": f"{blocks} sequences (greedy/sampling pairs) of the fused workload, each pair a separate "
+                  f"oracle call: float64 lm_head product (numpy/OpenBLAS, {cores} threads) + the "
+                  f"single-threaded C accept; {spent / blocks * 1e3:.0f} ms per sequence; host CPU: "
+                  f"{cpu_model()}",
+    }
+
+
+def main_fused(args) -> int:
+    """The fused verify workload: target logits formed from hidden states and
+    the lm_head weight inside the call."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import lossless_draft_verification_amd as L
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    log("generating the fused workload: " + W.FUSED_TEXT)
+    t0 = time.time()
+    case = W.fused_config()
+    log(f"generated in {time.time() - t0:.1f}s")
+    b, K, V, D, cap = case.b, case.K, case.V, case.D, case.softcap
+    M = b * (K + 1)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    h, w = bf(case.hidden), bf(case.weight)
+    d = torch.from_numpy(case.draft).to(dev)
+    x = torch.from_numpy(case.draft_tokens).to(dev)
+    temps = torch.from_numpy(case.temps).to(dev)
+    seeds = torch.from_numpy(case.seeds.view(np.int64)).to(dev)
+    out = L.AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                         torch.empty(b, K + 1, dtype=torch.int32, device=dev),
+                         p_draft=torch.empty(b, K, device=dev), q_draft=torch.empty(b, K, device=dev),
+                         argmax=torch.empty(b, K + 1, dtype=torch.int32, device=dev))
+    ws = torch.empty(L.fused_workspace_bytes(b, K, V, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k, evs=None):
+        L.set_stage_events(evs)
+        L.fused_mixed_accept(h, w, d, x, temps, seeds, softcap=cap, out=out, workspace=ws, stream=stream)
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(n):
+            fn(k)
+        end.record(stream)
+        torch.cuda.synchronize()
+        L.set_stage_events(None)
+        return start.elapsed_time(end)
+
+    log(f"warmup {args.warmup} fused steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"region 1: {args.steps} timed fused steps")
+    total_ms = timed(step, args.steps)
+    ms_per_step = total_ms / args.steps
+    log("region 2: the same steps with stage events")
+    names = ["lm_head_gemm", "tile_merge", "draft_row_pass", "scan", "residual_mass", "draw_token"]
+    evs = [mk_events(7) for _ in range(args.steps)]
+    staged_ms = timed(lambda k: step(k, evs[k]), args.steps)
+    stage = {nm: float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
+             for j, nm in enumerate(names)}
+    gemm_flops = 2.0 * M * D * V
+    achieved = gemm_flops / (stage["lm_head_gemm"] * 1e-3) / 1e12
+
+    n_all = out.n_accepted.cpu().numpy()
+    sidx = np.nonzero(case.temps > 0.0)[0]
+    n_s = n_all[sidx]
+    rejected = int(((n_s >= 0) & (n_s < K)).sum())
+    bonus = int((n_s == K).sum())
+    bs = len(sidx)
+    step_bytes = (V * D * 2 + M * D * 2 + bs * (K + 1) * V * 4 + bs * K * V * 4
+                  + rejected * 2 * V * 4 + bonus * SEG_BYTES)
+
+    reference = None
+    if not args.no_reference:
+        log("reference: hipBLASLt GEMM (bf16 in, fp32 out) + softcap + spec_mixed_accept")
+        h2 = h.view(M, D)
+        out_r = L.AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                               torch.empty(b, K + 1, dtype=torch.int32, device=dev),
+                               p_draft=torch.empty(b, K, device=dev), q_draft=torch.empty(b, K, device=dev),
+                               argmax=torch.empty(b, K + 1, dtype=torch.int32, device=dev))
+        ws_r = torch.empty(L.mixed_workspace_bytes(b, K, V, torch.float32), dtype=torch.uint8, device=dev)
+        try:
+            z = torch.mm(h2, w.t(), out_dtype=torch.float32)
+            gemm_kind = "torch.mm(bf16, bf16, out_dtype=float32)"
+        except Exception as e:                      # no fp32-output bf16 product in this torch
+            log(f"torch.mm out_dtype unavailable ({type(e).__name__}); reference GEMM in bf16 out")
+            z = None
+            gemm_kind = "torch.mm(bf16, bf16) -> bf16, then .float()"
+
+        def gemm():
+            if z is not None:
+                return torch.mm(h2, w.t(), out_dtype=torch.float32)
+            return torch.mm(h2, w.t()).float()
+
+        def ref_step(k):
+            zz = gemm()
+            zz.div_(cap).tanh_().mul_(cap)
+            L.mixed_accept(zz.view(b, K + 1, V), d, x, temps, seeds, out=out_r, workspace=ws_r, stream=stream)
+
+        for k in range(min(args.warmup, 20)):
+            ref_step(k)
+        n_ref = max(1, min(args.steps, 200))
+        ref_ms = timed(ref_step, n_ref) / n_ref
+        for k in range(5):
+            gemm()
+        gemm_ms = timed(lambda k: gemm(), n_ref) / n_ref
+        same = bool((out_r.n_accepted == out.n_accepted).all().item())
+        reference = {"unfused_ms_per_step": ref_ms, "unfused_blocks_per_s": b / (ref_ms * 1e-3),
+                     "library_gemm": gemm_kind, "library_gemm_ms": gemm_ms,
+                     "library_gemm_TFLOPs": gemm_flops / (gemm_ms * 1e-3) / 1e12,
+                     "same_accepted_lengths_as_fused": same}
+
+    result = {
+        "metric": "fused verify blocks/s (lm_head GEMM + verify), b=128 K=7 V=262144 D=3840",
+        "value": b / (ms_per_step * 1e-3),
+        "unit": "verify blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fused: " + W.FUSED_TEXT, "b": b, "K": K, "V": V, "D": D, "softcap": cap,
+                   "greedy_sequences": int((case.temps == 0.0).sum()), "sampling_sequences": bs,
+                   "step": "one spec_fused_mixed_accept call", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "lm_head_kernel", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": gemm_flops,
+                     "avg_launch_ms": stage["lm_head_gemm"]},
+        "step_hbm": {"algorithmic_bytes_per_step": step_bytes,
+                     "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                     "rejected_sequences": rejected, "bonus_sequences": bonus},
+        "stage_ms": stage,
+        "staged_ms_per_step": staged_ms / args.steps,
+        "reference": reference,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the fused oracle (budget {args.cpu_budget:.0f}s)")
+        result["cpu_baseline"] = cpu_baseline_fused(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +400,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--step", choices=["mixed", "split"], default="mixed")
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--fused", action="store_true",
+                    help="the fused verify workload (lm_head GEMM inside the call) instead of c5")
     ap.add_argument("--ragged", action="store_true",
                     help="mixed step with per-sequence draft lengths drawn uniformly from 0..K")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -234,6 +423,8 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.fused:
+        return main_fused(args)
 
     import numpy as np
     import torch

@@ -1235,14 +1235,16 @@ int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t 
         h_batch_stride % 8 != 0)
         return SPEC_EALIGN;
     if ((uintptr_t)draft % 4 != 0) return SPEC_EALIGN;
-    // the GEMM keeps 32-bit element offsets into hidden
-    if ((int64_t)(b - 1) * h_batch_stride + (int64_t)K * h_row_stride + D > (int64_t)INT_MAX) return SPEC_EINVAL;
+    // the GEMM addresses hidden and one weight tile with 32-bit byte offsets
+    const int64_t hspan = (int64_t)(b - 1) * h_batch_stride + (int64_t)K * h_row_stride + D;
+    if (hspan > (int64_t)INT_MAX || (int64_t)kLmBV * w_row_stride * 2 > (int64_t)INT_MAX) return SPEC_EINVAL;
     char *ws = (char *)workspace;
     float *logits = (float *)(ws + F.logits_off);
     LmArgs la = {};
     la.hidden = (const uint16_t *)hidden;
     la.hbs = h_batch_stride;
     la.hrs = h_row_stride;
+    la.hspan_bytes = (uint32_t)(hspan * 2);
     la.weight = (const uint16_t *)weight;
     la.wrs = w_row_stride;
     la.b = b;
@@ -1303,7 +1305,8 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, cons
     if (l_row_stride < V) return SPEC_EINVAL;
     if (!bf16_operand_ok(hidden, h_row_stride, D) || !bf16_operand_ok(weight, w_row_stride, D)) return SPEC_EALIGN;
     if ((uintptr_t)logits % 16 != 0 || l_row_stride % 4 != 0) return SPEC_EALIGN;
-    if ((int64_t)(rows - 1) * h_row_stride + D > (int64_t)INT_MAX) return SPEC_EINVAL;
+    const int64_t hspan = (int64_t)(rows - 1) * h_row_stride + D;
+    if (hspan > (int64_t)INT_MAX || (int64_t)kLmBV * w_row_stride * 2 > (int64_t)INT_MAX) return SPEC_EINVAL;
     const int64_t ntiles = ((int64_t)V + kLmBV - 1) / kLmBV;
     const int64_t th = ((int64_t)rows + kLmBH - 1) / kLmBH;
     if (ntiles * th > INT_MAX) return SPEC_EINVAL;
@@ -1311,6 +1314,7 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, cons
     la.hidden = (const uint16_t *)hidden;
     la.hbs = h_row_stride;
     la.hrs = 0;
+    la.hspan_bytes = (uint32_t)(hspan * 2);
     la.weight = (const uint16_t *)weight;
     la.wrs = w_row_stride;
     la.b = rows;

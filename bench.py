@@ -402,6 +402,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--fused", action="store_true",
                     help="the fused verify workload (lm_head GEMM inside the call) instead of c5")
+    ap.add_argument("--sharded", type=int, default=0, metavar="G",
+                    help="mixed step over G vocabulary shards in separate buffers")
     ap.add_argument("--ragged", action="store_true",
                     help="mixed step with per-sequence draft lengths drawn uniformly from 0..K")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -413,8 +415,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_rocprof:
         return summarize_rocprof(args.summarize_rocprof)
-    if args.ragged and args.step != "mixed":
-        print("--ragged needs --step mixed", file=sys.stderr)
+    if (args.ragged or args.sharded) and args.step != "mixed":
+        print("--ragged and --sharded need --step mixed", file=sys.stderr)
         return 2
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -477,6 +479,18 @@ def main() -> int:
 
     out_m = res(b, True, True)
     ws_m = torch.zeros(L.mixed_workspace_bytes(b, K, V, dt), dtype=torch.uint8, device=dev)
+    shard_copies, ws_sh, widths = None, None, None
+    if args.sharded:
+        G = args.sharded
+        unit = 8192 if V % (8192 * G) == 0 else 1
+        base = V // (unit * G) * unit
+        widths = [base] * (G - 1) + [V - base * (G - 1)]
+        cuts = np.cumsum([0] + widths)
+        shard_copies = [([t[:, :, a:c].contiguous() for a, c in zip(cuts[:-1], cuts[1:])],
+                         [d[:, :, a:c].contiguous() for a, c in zip(cuts[:-1], cuts[1:])]) for t, d in copies]
+        copies = copies[:1]
+        torch.cuda.empty_cache()
+        ws_sh = torch.zeros(L.sharded_workspace_bytes(widths, b, K, dt), dtype=torch.uint8, device=dev)
     out_g = res(max(bg, 1), False, True)
     ws_g = torch.zeros(L.workspace_bytes(max(bg, 1), K, V, dt, False), dtype=torch.uint8, device=dev)
     out_s = res(max(bs, 1), True, False)
@@ -484,8 +498,13 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step_mixed(k, evs=None):
-        t, d = copies[k % len(copies)]
         L.set_stage_events(evs)
+        if shard_copies is not None:
+            ts, ds = shard_copies[k % len(shard_copies)]
+            L.sharded_mixed_accept(ts, ds, x, temps, seeds, draft_lengths=klen, out=out_m, workspace=ws_sh,
+                                   stream=stream)
+            return
+        t, d = copies[k % len(copies)]
         L.mixed_accept(t, d, x, temps, seeds, draft_lengths=klen, out=out_m, workspace=ws_m, stream=stream)
 
     def step_split(k, gev=None, sev=None):
@@ -579,7 +598,8 @@ def main() -> int:
     else:
         dom, dom_bytes, dom_ms = "row_pass", bytes_greedy, stage["greedy_row_pass"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    wl_key = f"c{args.workload}_{args.step}" + ("_ragged" if args.ragged else "")
+    wl_key = (f"c{args.workload}_{args.step}" + ("_ragged" if args.ragged else "")
+              + (f"_sharded{args.sharded}" if args.sharded else ""))
     traffic = load_traffic(dom, wl_key)
 
     result = {
@@ -597,14 +617,16 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": f"c{args.workload}: {W.CONFIG_TEXT[args.workload]}" + (
-                "; per-sequence draft lengths uniform on 0..K (seeded)" if args.ragged else ""),
+                "; per-sequence draft lengths uniform on 0..K (seeded)" if args.ragged else "") + (
+                f"; vocabulary split into {args.sharded} shards of widths {widths}" if args.sharded else ""),
             "mean_draft_length": float(klen_np.mean()),
             "b": b, "K": K, "V": V, "temperature": case.T,
             "greedy_sequences": bg, "sampling_sequences": bs,
-            "step": ("one spec_mixed_accept call (per-sequence temperature 0 / 0.8)" if mixed else
+            "step": (f"one spec_sharded_mixed_accept call over {args.sharded} shards" if args.sharded else
+                     "one spec_mixed_accept call (per-sequence temperature 0 / 0.8)" if mixed else
                      "spec_greedy_accept over the greedy sequences + spec_sample_accept over the "
                      "sampling sequences, one stream"),
-            "input_copies_rotated": len(copies),
+            "input_copies_rotated": len(shard_copies) if shard_copies is not None else len(copies),
             "parallelism": "single GPU",
         },
         "roofline": {

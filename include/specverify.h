@@ -227,13 +227,51 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows,
                         float *logits, int64_t l_row_stride, void *hip_stream);
 
 /*
+ * Vocabulary-sharded verify: the target and draft logits arrive split by
+ * vocabulary column into G shards, as a tensor-parallel lm_head leaves them
+ * (shard g holds columns [col0_g, col0_g + shard_V[g]) of every row, col0_g
+ * the sum of the earlier widths), each shard in its own buffer.  The result
+ * is spec_mixed_accept's on the concatenated vocabulary (global token ids).
+ * Each shard runs the row pass and the residual pass on its own columns and
+ * contributes one statistics record per row -- (max, first argmax) or (max,
+ * sum of exp) -- and the draft-token logits it owns; the scan merges the G
+ * records of a row in shard order; the G shard totals of the draw's weights
+ * pick the shard that searches its columns for the drawn token.  On one GPU
+ * the shards are plain buffers; across GPUs the records (b*(2K+1)*16 B), the
+ * gathered logits (b*K*8 B) and the shard totals (b*G*8 B) are what would be
+ * all-gathered, and the drawn tokens what would be broadcast.
+ *
+ *   G               1 .. SPEC_MAX_SHARDS
+ *   target_shards   host array of G device pointers, shard g [b, K+1, shard_V[g]]
+ *   draft_shards    host array of G device pointers, shard g [b, K, shard_V[g]]
+ *   shard_V         host [G] widths (>= 1)
+ *   t_strides       host [2G]: batch and row element strides of each target shard
+ *   d_strides       host [2G]: same for the draft shards
+ *   workspace       spec_sharded_workspace_bytes(G, shard_V, b, K, dtype) bytes
+ * Other arguments and outputs as for spec_mixed_accept (V = sum of widths).
+ */
+#define SPEC_MAX_SHARDS 16
+
+size_t spec_sharded_workspace_bytes(int G, const int *shard_V, int b, int K, int dtype);
+
+int spec_sharded_mixed_accept(int G, const void *const *target_shards, const void *const *draft_shards,
+                              const int *shard_V, const int64_t *t_strides, const int64_t *d_strides,
+                              int dtype, const int32_t *draft_tokens, int b, int K,
+                              const double *temperatures, const int32_t *draft_lengths,
+                              const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens,
+                              float *p_draft, float *q_draft, int32_t *target_argmax,
+                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Profiling hook (not part of the accept semantics).  Registers, for the
  * calling host thread only, an array of n_events hipEvent_t handles.  While
  * registered, each accept call records events[0] before its first kernel and
  * events[k] after its k-th kernel on its stream (kernels: 1 row pass, 2 scan,
  * then for sampling and mixed calls 3 residual pass, 4 draw; for the fused
  * call 1 lm_head GEMM, 2 tile merge, 3 draft-row pass, 4 scan, 5 residual,
- * 6 draw), for every k < n_events; n_events = 2 brackets the first kernel.  Pass NULL / 0 to
+ * 6 draw; for the sharded call 1 row passes, 2 records + scan, 3 residual
+ * passes + shard selection, 4 draws), for every k < n_events; n_events = 2
+ * brackets the first kernel.  Pass NULL / 0 to
  * unregister.  Returns SPEC_OK.
  */
 int spec_set_stage_events(void *const *events, int n_events);

@@ -25,6 +25,7 @@ import torch
 
 __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_accept",
            "fused_mixed_accept", "lm_head_logits", "fused_workspace_bytes",
+           "sharded_mixed_accept", "sharded_workspace_bytes",
            "workspace_bytes", "mixed_workspace_bytes",
            "set_stage_events", "stream_copy", "library_path", "SpecError"]
 
@@ -74,6 +75,11 @@ def _load():
     lib.spec_fused_mixed_accept.restype = i32
     lib.spec_lm_head_logits.argtypes = [vp, i64, i32, vp, i64, i32, i32, f32, vp, i64, vp]
     lib.spec_lm_head_logits.restype = i32
+    lib.spec_sharded_workspace_bytes.argtypes = [i32, vp, i32, i32, i32]
+    lib.spec_sharded_workspace_bytes.restype = sz
+    lib.spec_sharded_mixed_accept.argtypes = [i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, sz, vp]
+    lib.spec_sharded_mixed_accept.restype = i32
     lib.spec_set_stage_events.argtypes = [vp, i32]
     lib.spec_set_stage_events.restype = i32
     lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
@@ -343,6 +349,75 @@ def lm_head_logits(hidden: torch.Tensor, weight: torch.Tensor, *, softcap: float
     rc = _lib.spec_lm_head_logits(hidden.data_ptr(), hidden.stride(0), rows, weight.data_ptr(), weight.stride(0),
                                   V, D, float(softcap), out.data_ptr(), out.stride(0),
                                   _stream_handle(hidden.device, stream))
+    _check(rc)
+    return out
+
+
+def sharded_workspace_bytes(shard_V: Sequence[int], b: int, K: int, dtype: torch.dtype) -> int:
+    G = len(shard_V)
+    arr = (ctypes.c_int * G)(*[int(v) for v in shard_V])
+    code = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
+    n = _lib.spec_sharded_workspace_bytes(G, ctypes.cast(arr, ctypes.c_void_p), b, K, code)
+    if n == 0:
+        raise ValueError(f"sizes out of range: G={G} b={b} K={K} widths={list(shard_V)}")
+    return n
+
+
+def sharded_mixed_accept(target_shards: Sequence[torch.Tensor], draft_shards: Sequence[torch.Tensor],
+                         draft_tokens: torch.Tensor, temperatures: torch.Tensor, seeds: torch.Tensor, *,
+                         draft_lengths: Optional[torch.Tensor] = None, out: Optional[AcceptResult] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> AcceptResult:
+    """Vocabulary-sharded mixed accept: shard g holds columns [col0_g,
+    col0_g + V_g) of every target row ([b, K+1, V_g]) and draft row
+    ([b, K, V_g]); the result is mixed_accept's on the concatenation."""
+    G = len(target_shards)
+    if G != len(draft_shards) or G < 1:
+        raise ValueError("need as many draft shards as target shards, at least one")
+    _on_gpu(*target_shards, *draft_shards, draft_tokens, temperatures, seeds)
+    t0 = target_shards[0]
+    b, K1 = t0.shape[0], t0.shape[1]
+    K = K1 - 1
+    widths = []
+    for t, d in zip(target_shards, draft_shards):
+        if t.dim() != 3 or d.dim() != 3 or t.stride(2) != 1 or d.stride(2) != 1:
+            raise ValueError("each shard needs its columns contiguous")
+        if t.shape[:2] != (b, K1) or d.shape != (b, K, t.shape[2]) or t.dtype != t0.dtype or d.dtype != t0.dtype:
+            raise ValueError("shards must be [b, K+1, V_g] / [b, K, V_g] with one dtype")
+        widths.append(int(t.shape[2]))
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    if temperatures.shape != (b,) or temperatures.dtype != torch.float64 or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be a contiguous float64 [b] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    if draft_lengths is not None:
+        _on_gpu(draft_lengths)
+        if (draft_lengths.shape != (b,) or draft_lengths.dtype != torch.int32
+                or not draft_lengths.is_contiguous()):
+            raise ValueError("draft_lengths must be a contiguous int32 [b] tensor")
+    dev = t0.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           p_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           q_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           argmax=torch.empty(b, K1, dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, sharded_workspace_bytes(widths, b, K, t0.dtype), dev)
+    tp = (ctypes.c_void_p * G)(*[t.data_ptr() for t in target_shards])
+    dp = (ctypes.c_void_p * G)(*[d.data_ptr() for d in draft_shards])
+    vw = (ctypes.c_int * G)(*widths)
+    ts = (ctypes.c_int64 * (2 * G))(*[x for t in target_shards for x in (t.stride(0), t.stride(1))])
+    ds = (ctypes.c_int64 * (2 * G))(*[x for d in draft_shards for x in (d.stride(0), d.stride(1))])
+    rc = _lib.spec_sharded_mixed_accept(
+        G, ctypes.cast(tp, ctypes.c_void_p), ctypes.cast(dp, ctypes.c_void_p), ctypes.cast(vw, ctypes.c_void_p),
+        ctypes.cast(ts, ctypes.c_void_p), ctypes.cast(ds, ctypes.c_void_p), _dtype_code(t0),
+        draft_tokens.data_ptr(), b, K, temperatures.data_ptr(),
+        draft_lengths.data_ptr() if draft_lengths is not None else None, seeds.data_ptr(),
+        out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.p_draft.data_ptr() if out.p_draft is not None else None,
+        out.q_draft.data_ptr() if out.q_draft is not None else None,
+        out.argmax.data_ptr() if out.argmax is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
     _check(rc)
     return out
 

@@ -78,6 +78,8 @@ struct DrawPlan {
     float Lt_hi, Lt_lo; // log2 of the target row's sum at Mt, split hi + lo
     float Ld_hi, Ld_lo; // same for the draft row
     double St;          // target row sum at Mt
+    int32_t shard;      // vocabulary-sharded call: the shard that draws
+    double t_local;     // and the draw's target mass inside that shard
 };
 
 __host__ __device__ constexpr int elems_per_vec(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
@@ -287,6 +289,9 @@ struct Ctx {
     double T_uniform;                  // the call's temperature when temps is NULL
     const int32_t *klen;               // per-sequence draft lengths [b], or NULL (all K)
     int row_lo, rpl;                   // row pass: partial rows row_lo .. row_lo+rpl-1 of each sequence
+    int shard_id;                      // vocabulary-sharded call: this launch's shard, else -1
+    int32_t col0;                      // first vocabulary column of the shard (0 unsharded)
+    const float *zx;                   // sharded scan: gathered [b, K, 2] z_t(x_i), z_d(x_i), or NULL
     const int32_t *x;                  // draft tokens [b, K]
     const uint64_t *seeds;             // [b]
     int32_t *n_out, *tok;              // [b], [b, K+1]
@@ -466,8 +471,13 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         x = c.x[(int64_t)s * K + lane];
         tok_bad = x < 0 || x >= V;
         if (rule == kRuleSample && !tok_bad) {
-            zt = elem_at<DT>(row_ptr<DT>(c.target, c.tbs, c.trs, s, lane), x);
-            zd = elem_at<DT>(row_ptr<DT>(c.draft, c.dbs, c.drs, s, lane), x);
+            if (c.zx) {
+                zt = c.zx[((int64_t)s * K + lane) * 2];
+                zd = c.zx[((int64_t)s * K + lane) * 2 + 1];
+            } else {
+                zt = elem_at<DT>(row_ptr<DT>(c.target, c.tbs, c.trs, s, lane), x);
+                zd = elem_at<DT>(row_ptr<DT>(c.draft, c.dbs, c.drs, s, lane), x);
+            }
         }
     }
 
@@ -785,6 +795,8 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
     const double rm_first = r0 < min(nres, r0 + rper) ? rm[r0] : 0.0;
     const DrawPlan pl = c.plan[s];
     if (pl.mode == kModeNone) return;
+    const bool sharded = c.shard_id >= 0;
+    if (sharded && pl.shard != c.shard_id) return;
     float c_hi, c_lo;
     double c64;
     split_scale(pl.T, c_hi, c_lo, c64);
@@ -801,7 +813,7 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
     double local = 0.0, excl, incl, total;
     for (int j = j0; j < j1; ++j) local += (resid && j == r0) ? rm_first : seg_mass(j);
     block_scan(local, excl, incl, total, sw);
-    if (resid && !(total > 0.0)) {                     // zero residual mass: draw from p_n
+    if (!sharded && resid && !(total > 0.0)) {         // zero residual mass: draw from p_n
         resid = false;
         nsg = nseg;
         per = (nsg + kBlock - 1) / kBlock;
@@ -811,7 +823,9 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
         for (int j = j0; j < j1; ++j) local += seg_mass(j);
         block_scan(local, excl, incl, total, sw);
     }
-    const double tt = pl.u2 * total;                   // u2 < 1: tt < total when total > 0
+    // u2 < 1: tt < total when total > 0.  A shard draws at the mass the shard
+    // selection left inside it, kept below this shard's own total.
+    const double tt = sharded ? fmin(pl.t_local, nextafter(total, 0.0)) : pl.u2 * total;
     if (t == 0) {
         sSeg = 0;
         sOff = 0.0;
@@ -862,7 +876,7 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
     if (t == 0) {
         int32_t y = sY >= 0 ? sY : sLastPos;
         if (y < 0) y = (int32_t)min((int64_t)V - 1, (int64_t)seg * (resid ? rseg_elems(DT) : seg_elems(DT)));
-        c.tok[(int64_t)s * (K + 1) + pl.slot] = y;
+        c.tok[(int64_t)s * (K + 1) + pl.slot] = y + c.col0;
     }
 }
 
@@ -998,6 +1012,9 @@ int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L
     c.rps = L.rps;
     c.row_lo = 0;
     c.rpl = L.rps;
+    c.shard_id = -1;
+    c.col0 = 0;
+    c.zx = nullptr;
     c.part = (Partial *)(ws + L.part_off);
     const bool draws = kind != kCallGreedy;
     c.plan = draws ? (DrawPlan *)(ws + L.plan_off) : nullptr;
@@ -1067,6 +1084,8 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
     stage_mark(6, st);
     return SPEC_OK;
 }
+
+#include "vocab_sharded.inc"
 
 bool bf16_operand_ok(const void *p, int64_t stride, int D) {
     return p && (uintptr_t)p % 16 == 0 && stride >= D && stride % 8 == 0;
@@ -1288,6 +1307,9 @@ int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t 
     c.rps = L.rps;
     c.row_lo = 0;
     c.rpl = L.rps;
+    c.shard_id = -1;
+    c.col0 = 0;
+    c.zx = nullptr;
     c.part = (Partial *)(ws + L.part_off);
     c.plan = (DrawPlan *)(ws + L.plan_off);
     c.rmass = (double *)(ws + L.rmass_off);
@@ -1332,6 +1354,83 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, cons
     la.write_all = 1;
     hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(ntiles * th)), dim3(kLmThreads), 0, (hipStream_t)hip_stream, la);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+size_t spec_sharded_workspace_bytes(int G, const int *shard_V, int b, int K, int dtype) {
+    ShardedLayout S;
+    if (!make_sharded_layout(G, shard_V, b, K, dtype, S)) return 0;
+    return S.total;
+}
+
+int spec_sharded_mixed_accept(int G, const void *const *target_shards, const void *const *draft_shards,
+                              const int *shard_V, const int64_t *t_strides, const int64_t *d_strides, int dtype,
+                              const int32_t *draft_tokens, int b, int K, const double *temperatures,
+                              const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted,
+                              int32_t *tokens, float *p_draft, float *q_draft, int32_t *target_argmax,
+                              void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
+    ShardedLayout S;
+    if (!make_sharded_layout(G, shard_V, b, K, dtype, S)) return SPEC_EINVAL;
+    if (!target_shards || !draft_shards || !t_strides || !d_strides) return SPEC_EINVAL;
+    if (!draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
+    if (workspace_bytes < S.total) return SPEC_EINVAL;
+    const int es = elem_bytes(dtype);
+    char *ws = (char *)workspace;
+    Ctx cg[kMaxShards];
+    bool vec[kMaxShards];
+    int32_t col0 = 0;
+    for (int g = 0; g < G; ++g) {
+        const void *tp = target_shards[g], *dp = draft_shards[g];
+        const int64_t tbs = t_strides[2 * g], trs = t_strides[2 * g + 1];
+        const int64_t dbs = d_strides[2 * g], drs = d_strides[2 * g + 1];
+        if (!tp || !dp) return SPEC_EINVAL;
+        if (trs < shard_V[g] || tbs < 0 || drs < shard_V[g] || dbs < 0) return SPEC_EINVAL;
+        if ((uintptr_t)tp % es != 0 || (uintptr_t)dp % es != 0) return SPEC_EALIGN;
+        Ctx c = {};
+        c.target = tp;
+        c.draft = dp;
+        c.tbs = tbs;
+        c.trs = trs;
+        c.dbs = dbs;
+        c.drs = drs;
+        c.K = K;
+        c.V = shard_V[g];
+        c.nseg = S.nseg[g];
+        c.nres = S.nres[g];
+        c.rps = S.rps;
+        c.row_lo = 0;
+        c.rpl = S.rps;
+        c.temps = temperatures;
+        c.klen = draft_lengths;
+        c.x = draft_tokens;
+        c.seeds = seeds;
+        c.n_out = n_accepted;
+        c.tok = tokens;
+        c.part = (Partial *)(ws + S.part_off[g]);
+        c.rmass = (double *)(ws + S.rmass_off[g]);
+        c.plan = (DrawPlan *)(ws + S.plan_off);
+        c.shard_id = g;
+        c.col0 = col0;
+        c.zx = nullptr;
+        cg[g] = c;
+        vec[g] = rows_vector_aligned(tp, es, tbs, trs) && rows_vector_aligned(dp, es, dbs, drs);
+        col0 += shard_V[g];
+    }
+    // The scan's view: one record per shard in place of segments, the gathered
+    // draft-token logits, the whole vocabulary for the token range check.
+    Ctx call = cg[0];
+    call.V = col0;
+    call.nseg = G;
+    call.part = (Partial *)(ws + S.rec_off);
+    call.zx = (const float *)(ws + S.zx_off);
+    call.shard_id = -1;
+    call.col0 = 0;
+    call.p_out = p_draft;
+    call.q_out = q_draft;
+    call.am = target_argmax;
+    hipStream_t st = (hipStream_t)hip_stream;
+    return dtype == SPEC_BF16 ? launch_sharded<SPEC_BF16>(cg, vec, call, b, S, ws, st)
+                              : launch_sharded<SPEC_F32>(cg, vec, call, b, S, ws, st);
 }
 
 }  // extern "C"

@@ -164,6 +164,35 @@ def test_lm_head_logits_validation(lib):
     assert f(256, 128, 4, 512, 128, 1000, 128, 0.0, 1024, 1002, None) == 3
 
 
+def test_sharded_argument_validation(lib):
+    import ctypes
+    widths = (ctypes.c_int * 3)(1000, 2000, 17)
+    assert lib.spec_sharded_workspace_bytes(3, widths, 4, 7, 1) > 0
+    assert lib.spec_sharded_workspace_bytes(0, widths, 4, 7, 1) == 0
+    assert lib.spec_sharded_workspace_bytes(17, widths, 4, 7, 1) == 0            # more than SPEC_MAX_SHARDS
+    bad = (ctypes.c_int * 2)(1000, 0)
+    assert lib.spec_sharded_workspace_bytes(2, bad, 4, 7, 1) == 0                # empty shard
+    assert lib.spec_sharded_workspace_bytes(3, widths, 4, 33, 1) == 0
+    ptrs = (ctypes.c_void_p * 3)(256, 512, 768)
+    strides = (ctypes.c_int64 * 6)(8 * 1000, 1000, 8 * 2000, 2000, 8 * 17, 17)
+    f = lib.spec_sharded_mixed_accept
+    args = [3, ptrs, ptrs, widths, strides, strides, 1, 16, 4, 7, 16, None, 16, 16, 16, None, None, None, 4096,
+            1 << 30, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=5) == 2                       # dtype
+    assert call(a1=None) == 1
+    assert call(a10=None) == 1                   # temperatures
+    assert call(a19=64) == 1                     # workspace too small
+    short = (ctypes.c_int64 * 6)(8 * 1000, 999, 8 * 2000, 2000, 8 * 17, 17)
+    assert call(a4=short) == 1                   # row stride below the shard width
+    odd = (ctypes.c_void_p * 3)(257, 512, 768)
+    assert call(a1=odd) == 3                     # bf16 shard not 2-byte aligned
+
+
 def test_stream_copy_validation(lib):
     assert lib.spec_stream_copy(None, 16, 16, None) == 1
     assert lib.spec_stream_copy(16, 16, 15, None) == 1

@@ -347,3 +347,69 @@ def fused_config(b: int = 128, K: int = 7, V: int = 262144, D: int = 3840) -> Fu
     seed 6001); smaller b / V / D keep the recipe."""
     rules = np.array([GREEDY] * (b // 2) + [SAMPLING] * (b - b // 2), np.int32)
     return make_fused_case("fused", b=b, K=K, V=V, D=D, softcap=30.0, rule=rules, T=0.8, seed=6001)
+
+
+# ---------------------------------------------------------------------------
+# Draft-side block decode inputs: the parallel backbone's base logits, the
+# rank-r Markov head tables and the confidence head (rank 256, the Gemma-4
+# drafter's markov_rank, "dspark-mlx 0.1.0" wheel diff, arch/gemma4.py).
+#
+#   base     float32 [b, K, V] iid N(0, scale^2)
+#   w1       bf16 [V, r] iid N(0, 1)                 (previous-token features)
+#   w2       bf16 [V, r] iid N(0, (gain / sqrt r)^2) (the table, row v = entry v)
+#   hidden   bf16 [b, K, D] iid N(0, 1), conf_w bf16 [D + r] iid N(0, 1/(D + r)),
+#            conf_b = 1.0
+#   anchors  uniform tokens; temps 0 (greedy) or T per sequence; seeds = index
+
+
+@dataclass
+class MarkovCase:
+    name: str
+    b: int
+    K: int
+    V: int
+    r: int
+    D: int
+    base: np.ndarray
+    anchors: np.ndarray
+    w1: np.ndarray
+    w2: np.ndarray
+    hidden: np.ndarray
+    conf_w: np.ndarray
+    conf_b: float
+    temps: np.ndarray
+    seeds: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+
+def make_markov_case(name: str, *, b: int, K: int, V: int, r: int = 256, D: int = 64,
+                     scale: float = 3.0, gain: float = 3.0, rule: Union[int, Sequence[int]] = SAMPLING,
+                     T: float = 0.8, seed: int = 0) -> MarkovCase:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rules = np.full(b, int(rule), np.int32) if np.isscalar(rule) else np.asarray(rule, np.int32)
+    base = np.empty((b, K, V), np.float32)
+    for s in range(b):
+        base[s] = rng.standard_normal((K, V), dtype=np.float32) * np.float32(scale)
+    w1 = np.empty((V, r), np.uint16)
+    w2 = np.empty((V, r), np.uint16)
+    slab = max(1, (1 << 24) // r)
+    for v0 in range(0, V, slab):
+        v1 = min(V, v0 + slab)
+        w1[v0:v1] = bf16_bits(rng.standard_normal((v1 - v0, r), dtype=np.float32))
+        w2[v0:v1] = bf16_bits(rng.standard_normal((v1 - v0, r), dtype=np.float32) * np.float32(gain / np.sqrt(r)))
+    hidden = bf16_bits(rng.standard_normal((b, K, D), dtype=np.float32))
+    conf_w = bf16_bits(rng.standard_normal(D + r, dtype=np.float32) * np.float32(1.0 / np.sqrt(D + r)))
+    anchors = rng.integers(0, V, b).astype(np.int32)
+    temps = np.where(rules == GREEDY, 0.0, float(T))
+    return MarkovCase(name, b, K, V, r, D, base, anchors, w1, w2, hidden, conf_w, 1.0, temps,
+                      np.arange(b, dtype=np.uint64), {"seed": seed})
+
+
+MARKOV_TEXT = ("b=128 K=7 V=262144 r=256 D=3840: float32 base logits N(0,3^2), bf16 Markov tables "
+               "W1 [V,r] N(0,1) and W2 [V,r] N(0,(3/16)^2), confidence head on [hidden; u], "
+               "rows 0..63 greedy / 64..127 sampled at T=0.8")
+
+
+def markov_config(b: int = 128, K: int = 7, V: int = 262144, r: int = 256, D: int = 3840) -> MarkovCase:
+    rules = np.array([GREEDY] * (b // 2) + [SAMPLING] * (b - b // 2), np.int32)
+    return make_markov_case("markov", b=b, K=K, V=V, r=r, D=D, rule=rules, T=0.8, seed=7001)

@@ -391,6 +391,116 @@ def main_fused(args) -> int:
     return 0
 
 
+def cpu_baseline_markov(case, budget_s: float):
+    """Time the Markov block-decode oracle on small batches of the workload."""
+    import numpy as np
+    import oracle.markov as OM
+    spent, blocks, k = 0.0, 0, 0
+    while k == 0 or (spent < budget_s and 2 * k + 2 <= case.b):
+        idx = [2 * k, 2 * k + 1]
+        t0 = time.perf_counter()
+        OM.block_decode(case.base[idx], case.anchors[idx], case.w1, case.w2, case.temps[idx], case.seeds[idx],
+                        hidden=case.hidden[idx], conf_w=case.conf_w, conf_b=case.conf_b, threshold=0.6)
+        spent += time.perf_counter() - t0
+        blocks += 2
+        k += 1
+    return {"value": blocks / spent, "unit": "draft blocks/s", "cores": os.cpu_count() or 1, "kind": "oracle",
+            "sample": f"{blocks} sequences of the Markov workload in pairs (one greedy, one sampled): float64 "
+                      f"correction by numpy, C-oracle draws; {spent / blocks * 1e3:.0f} ms per sequence; "
+                      f"host CPU: {cpu_model()}"}
+
+
+def main_markov(args) -> int:
+    """The draft-side block decode with the Markov head (the step that
+    produces the verify's draft block)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import lossless_draft_verification_amd as L
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    log("generating the Markov workload: " + W.MARKOV_TEXT)
+    t0 = time.time()
+    case = W.markov_config()
+    log(f"generated in {time.time() - t0:.1f}s")
+    b, K, V, r, D = case.b, case.K, case.V, case.r, case.D
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = torch.from_numpy(case.base).to(dev)
+    anchors = torch.from_numpy(case.anchors).to(dev)
+    w1, w2, hid, cw = bf(case.w1), bf(case.w2), bf(case.hidden), bf(case.conf_w)
+    temps = torch.from_numpy(case.temps).to(dev)
+    seeds = torch.from_numpy(case.seeds.view(np.int64)).to(dev)
+    out = L.DraftBlock(torch.empty(b, K, dtype=torch.int32, device=dev),
+                       torch.empty(b, K, V, dtype=torch.float32, device=dev),
+                       torch.empty(b, K, dtype=torch.float32, device=dev), torch.empty(b, dtype=torch.int32, device=dev))
+    ws = torch.empty(L.markov_workspace_bytes(b, K, V, r), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k, evs=None):
+        L.set_stage_events(evs)
+        L.markov_block_decode(base, anchors, w1, w2, temps, seeds, hidden=hid, conf_w=cw, conf_b=case.conf_b,
+                              threshold=0.6, out=out, workspace=ws, stream=stream)
+
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(n):
+            fn(k)
+        end.record(stream)
+        torch.cuda.synchronize()
+        L.set_stage_events(None)
+        return start.elapsed_time(end)
+
+    log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    total_ms = timed(step, args.steps)
+    ms = total_ms / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        for q in e:
+            q.record(stream)
+    staged = timed(lambda k: step(k, evs[k]), args.steps)
+    loop_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    conf_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # per position: the W2 table, the base row and the corrected row of every
+    # sequence, the gathered W1 rows; then one bonus-free draw segment per
+    # sampled sequence (16 KiB fp32)
+    bs = int((case.temps > 0.0).sum())
+    per_pos = V * r * 2 + b * V * 4 * 2 + b * r * 2 + bs * SEG_BYTES
+    loop_bytes = K * per_pos
+    achieved = loop_bytes / (loop_ms * 1e-3) / 1e9
+    result = {
+        "metric": "draft blocks/s (Markov-head block decode), b=128 K=7 V=262144 r=256",
+        "value": b / (ms * 1e-3), "unit": "draft blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "markov: " + W.MARKOV_TEXT, "b": b, "K": K, "V": V, "r": r, "D": D,
+                   "confidence_threshold": 0.6, "step": "one spec_markov_block_decode call",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "position loop (lm_head_kernel in gather mode + merge + pick + draw)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms},
+        "stage_ms": {"position_loop": loop_ms, "confidence": conf_ms},
+        "staged_ms_per_step": staged / args.steps,
+        "mean_draft_length": float(out.lengths.float().mean().item()),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the Markov oracle (budget {args.cpu_budget:.0f}s)")
+        result["cpu_baseline"] = cpu_baseline_markov(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +510,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--step", choices=["mixed", "split"], default="mixed")
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--markov", action="store_true",
+                    help="the draft-side Markov block decode instead of the verify")
     ap.add_argument("--fused", action="store_true",
                     help="the fused verify workload (lm_head GEMM inside the call) instead of c5")
     ap.add_argument("--sharded", type=int, default=0, metavar="G",
@@ -427,6 +539,8 @@ def main() -> int:
         return copy_calibration(args.copy_calibration)
     if args.fused:
         return main_fused(args)
+    if args.markov:
+        return main_markov(args)
 
     import numpy as np
     import torch

@@ -263,6 +263,54 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * Draft-side block decode with the Markov head -- the step that produces the
+ * verify's draft block.  The parallel backbone's base logits L [b, K, V]
+ * (float32) get, position by position, a rank-r correction conditioned on
+ * the previous token ("dspark-mlx 0.1.0" README "How it works": a rank-256
+ * previous-token correction sampled sequentially; "mlx-dspark 0.0.1"
+ * __init__.py; the ds4 drafter card, "Files": the markov_w2 table read in
+ * full per draft position):
+ *
+ *   u_i = w1[x_{i-1}]  (x_{-1} = anchors[s]),   q_i = L_i + w2 u_i,
+ *   x_i = first argmax of q_i (temperature 0) or the inverse-CDF draw from
+ *         softmax(q_i / T) at t = U R, U = Philox(seed, position i, row s, tag 2),
+ *
+ * the correction formed on the matrix cores (bf16 tables, fp32 sums).  With
+ * hidden and conf_w, also the confidence head
+ * conf_i = sigmoid(conf_w . [hidden_i ; u_i] + conf_b) and the draft length
+ * = leading positions with conf_i >= threshold (K when threshold <= 0), the
+ * draft_lengths input of spec_mixed_accept.
+ *
+ *   base            float32 [b, K, V] (element strides)
+ *   anchors         int32 [b] (device): the last committed token
+ *   w1, w2          bf16 [V, r] (device), r a positive multiple of 64, row
+ *                   strides multiples of 8, 16-byte aligned; w2 row v holds the
+ *                   table's entries for vocabulary entry v
+ *   temperatures    double [b]: 0 greedy, > 0 sampling, else tokens -1
+ *   seeds           uint64 [b]
+ *   hidden          bf16 [b, K, D] and conf_w bf16 [D + r], or NULL (no confidence)
+ *   tokens          int32 [b, K] out; -1 from a position whose previous token
+ *                   or logits are invalid on
+ *   draft_logits    float32 [b, K, V] out (the corrected q_i), 16-byte aligned,
+ *                   strides multiples of 4
+ *   confidence      float [b, K] out or NULL; lengths int32 [b] out or NULL
+ *   workspace       spec_markov_workspace_bytes(b, K, V, r) bytes, 256-byte aligned
+ * Four kernels per position (GEMM with epilogue, tile merge, pick, draw), then
+ * one confidence kernel.
+ */
+size_t spec_markov_workspace_bytes(int b, int K, int V, int r);
+
+int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64_t base_row_stride,
+                             const int32_t *anchors, const void *w1, int64_t w1_row_stride,
+                             const void *w2, int64_t w2_row_stride, int r, int b, int K, int V,
+                             const double *temperatures, const uint64_t *seeds,
+                             const void *hidden, int64_t h_batch_stride, int64_t h_row_stride, int D,
+                             const void *conf_w, float conf_b, float threshold,
+                             int32_t *tokens, float *draft_logits, int64_t q_batch_stride,
+                             int64_t q_row_stride, float *confidence, int32_t *lengths,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Profiling hook (not part of the accept semantics).  Registers, for the
  * calling host thread only, an array of n_events hipEvent_t handles.  While
  * registered, each accept call records events[0] before its first kernel and
@@ -270,8 +318,9 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
  * then for sampling and mixed calls 3 residual pass, 4 draw; for the fused
  * call 1 lm_head GEMM, 2 tile merge, 3 draft-row pass, 4 scan, 5 residual,
  * 6 draw; for the sharded call 1 row passes, 2 records + scan, 3 residual
- * passes + shard selection, 4 draws), for every k < n_events; n_events = 2
- * brackets the first kernel.  Pass NULL / 0 to
+ * passes + shard selection, 4 draws; for the Markov block decode 1 after all
+ * positions, 2 after the confidence), for every k < n_events; n_events = 2
+ * brackets the first kernel (the whole position loop for the Markov decode).  Pass NULL / 0 to
  * unregister.  Returns SPEC_OK.
  */
 int spec_set_stage_events(void *const *events, int n_events);

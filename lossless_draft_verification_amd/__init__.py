@@ -26,6 +26,7 @@ import torch
 __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_accept",
            "fused_mixed_accept", "lm_head_logits", "fused_workspace_bytes",
            "sharded_mixed_accept", "sharded_workspace_bytes",
+           "DraftBlock", "markov_block_decode", "markov_workspace_bytes",
            "workspace_bytes", "mixed_workspace_bytes",
            "set_stage_events", "stream_copy", "library_path", "SpecError"]
 
@@ -80,6 +81,11 @@ def _load():
     lib.spec_sharded_mixed_accept.argtypes = [i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, sz, vp]
     lib.spec_sharded_mixed_accept.restype = i32
+    lib.spec_markov_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_markov_workspace_bytes.restype = sz
+    lib.spec_markov_block_decode.argtypes = [vp, i64, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, i64,
+                                             i64, i32, vp, f32, f32, vp, vp, i64, i64, vp, vp, vp, sz, vp]
+    lib.spec_markov_block_decode.restype = i32
     lib.spec_set_stage_events.argtypes = [vp, i32]
     lib.spec_set_stage_events.restype = i32
     lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
@@ -417,6 +423,83 @@ def sharded_mixed_accept(target_shards: Sequence[torch.Tensor], draft_shards: Se
         out.p_draft.data_ptr() if out.p_draft is not None else None,
         out.q_draft.data_ptr() if out.q_draft is not None else None,
         out.argmax.data_ptr() if out.argmax is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+@dataclass
+class DraftBlock:
+    """Result of markov_block_decode (device tensors).
+
+    tokens      [b, K] int32 draft tokens (-1 from the first invalid position on)
+    logits      [b, K, V] float32 corrected draft logits q_i (the verify's draft block)
+    confidence  [b, K] float32 confidence of each position, or None
+    lengths     [b] int32 draft length from the confidence threshold, or None
+    """
+    tokens: torch.Tensor
+    logits: torch.Tensor
+    confidence: Optional[torch.Tensor] = None
+    lengths: Optional[torch.Tensor] = None
+
+
+def markov_workspace_bytes(b: int, K: int, V: int, r: int) -> int:
+    n = _lib.spec_markov_workspace_bytes(b, K, V, r)
+    if n == 0:
+        raise ValueError(f"sizes out of range: b={b} K={K} V={V} r={r} (r a multiple of 64)")
+    return n
+
+
+def markov_block_decode(base: torch.Tensor, anchors: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+                        temperatures: torch.Tensor, seeds: torch.Tensor, *, hidden: Optional[torch.Tensor] = None,
+                        conf_w: Optional[torch.Tensor] = None, conf_b: float = 0.0, threshold: float = 0.0,
+                        out: Optional[DraftBlock] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> DraftBlock:
+    """Draft-side block decode with the Markov head: q_i = base_i + W2 W1[x_{i-1}]
+    (x_{-1} = anchor), x_i = argmax q_i (temperature 0) or a draw from
+    softmax(q_i / T); base float32 [b, K, V], w1 and w2 bf16 [V, r].  With
+    hidden [b, K, D] and conf_w [D + r] (bf16) also the confidence
+    sigmoid(conf_w . [h_i ; W1[x_{i-1}]] + conf_b) and the draft length."""
+    _on_gpu(base, anchors, w1, w2, temperatures, seeds)
+    if base.dim() != 3 or base.dtype != torch.float32 or base.stride(2) != 1:
+        raise ValueError("base must be float32 [b, K, V] with V contiguous")
+    b, K, V = base.shape
+    if w1.dim() != 2 or w1.dtype != torch.bfloat16 or w1.stride(1) != 1 or w1.shape[0] != V:
+        raise ValueError("w1 must be bf16 [V, r] with r contiguous")
+    r = w1.shape[1]
+    if w2.shape != (V, r) or w2.dtype != torch.bfloat16 or w2.stride(1) != 1:
+        raise ValueError("w2 must be bf16 [V, r] with r contiguous")
+    if anchors.shape != (b,) or anchors.dtype != torch.int32 or not anchors.is_contiguous():
+        raise ValueError("anchors must be a contiguous int32 [b] tensor")
+    if temperatures.shape != (b,) or temperatures.dtype != torch.float64 or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be a contiguous float64 [b] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    want_conf = hidden is not None and conf_w is not None
+    D = 0
+    if want_conf:
+        _on_gpu(hidden, conf_w)
+        if hidden.dim() != 3 or hidden.shape[:2] != (b, K) or hidden.dtype != torch.bfloat16 or hidden.stride(2) != 1:
+            raise ValueError("hidden must be bf16 [b, K, D] with D contiguous")
+        D = hidden.shape[2]
+        if conf_w.shape != (D + r,) or conf_w.dtype != torch.bfloat16 or not conf_w.is_contiguous():
+            raise ValueError("conf_w must be a contiguous bf16 [D + r] tensor")
+    dev = base.device
+    if out is None:
+        out = DraftBlock(torch.empty(b, K, dtype=torch.int32, device=dev),
+                         torch.empty(b, K, (V + 3) // 4 * 4, dtype=torch.float32, device=dev)[:, :, :V],
+                         torch.empty(b, K, dtype=torch.float32, device=dev) if want_conf else None,
+                         torch.empty(b, dtype=torch.int32, device=dev) if want_conf else None)
+    ws = _workspace(workspace, markov_workspace_bytes(b, K, V, r), dev)
+    q = out.logits
+    rc = _lib.spec_markov_block_decode(
+        base.data_ptr(), base.stride(0), base.stride(1), anchors.data_ptr(), w1.data_ptr(), w1.stride(0),
+        w2.data_ptr(), w2.stride(0), r, b, K, V, temperatures.data_ptr(), seeds.data_ptr(),
+        hidden.data_ptr() if want_conf else None, hidden.stride(0) if want_conf else 0,
+        hidden.stride(1) if want_conf else 0, D, conf_w.data_ptr() if want_conf else None, float(conf_b),
+        float(threshold), out.tokens.data_ptr(), q.data_ptr(), q.stride(0), q.stride(1),
+        out.confidence.data_ptr() if out.confidence is not None else None,
+        out.lengths.data_ptr() if out.lengths is not None else None,
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
     _check(rc)
     return out

@@ -1061,7 +1061,7 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
     stage_mark(1, st);
     const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg;
     hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c,
-                       (const Partial *)la.tpart, F.ntiles, c.K + 1, b);
+                       (const Partial *)la.tpart, F.ntiles, c.K + 1, b, 0);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(2, st);
     // draft rows only (partial rows K+1 .. 2K)
@@ -1086,6 +1086,7 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
 }
 
 #include "vocab_sharded.inc"
+#include "markov_draft.inc"
 
 bool bf16_operand_ok(const void *p, int64_t stride, int D) {
     return p && (uintptr_t)p % 16 == 0 && stride >= D && stride % 8 == 0;
@@ -1431,6 +1432,115 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
     hipStream_t st = (hipStream_t)hip_stream;
     return dtype == SPEC_BF16 ? launch_sharded<SPEC_BF16>(cg, vec, call, b, S, ws, st)
                               : launch_sharded<SPEC_F32>(cg, vec, call, b, S, ws, st);
+}
+
+size_t spec_markov_workspace_bytes(int b, int K, int V, int r) {
+    MarkovLayout L;
+    if (!make_markov_layout(b, K, V, r, L)) return 0;
+    return L.total;
+}
+
+int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64_t base_row_stride,
+                             const int32_t *anchors, const void *w1, int64_t w1_row_stride, const void *w2,
+                             int64_t w2_row_stride, int r, int b, int K, int V, const double *temperatures,
+                             const uint64_t *seeds, const void *hidden, int64_t h_batch_stride,
+                             int64_t h_row_stride, int D, const void *conf_w, float conf_b, float threshold,
+                             int32_t *tokens, float *draft_logits, int64_t q_batch_stride, int64_t q_row_stride,
+                             float *confidence, int32_t *lengths, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+    MarkovLayout L;
+    if (!make_markov_layout(b, K, V, r, L)) return SPEC_EINVAL;
+    if (!base || !anchors || !w1 || !w2 || !temperatures || !seeds || !tokens || !draft_logits || !workspace)
+        return SPEC_EINVAL;
+    if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
+    if (base_row_stride < V || base_batch_stride < 0 || q_row_stride < V || q_batch_stride < 0) return SPEC_EINVAL;
+    if (!(threshold == threshold) || !(conf_b == conf_b)) return SPEC_EINVAL;
+    const bool want_conf = confidence != nullptr;
+    if (want_conf && (!hidden || !conf_w || D < 1 || h_row_stride < D || h_batch_stride < 0)) return SPEC_EINVAL;
+    if ((uintptr_t)base % 4) return SPEC_EALIGN;
+    if ((uintptr_t)draft_logits % 16 || q_row_stride % 4 || q_batch_stride % 4) return SPEC_EALIGN;
+    if (!bf16_operand_ok(w1, w1_row_stride, r) || !bf16_operand_ok(w2, w2_row_stride, r)) return SPEC_EALIGN;
+    if (want_conf && ((uintptr_t)hidden % 2 || (uintptr_t)conf_w % 2)) return SPEC_EALIGN;
+    const int64_t w1span = (int64_t)(V - 1) * w1_row_stride + r;
+    if (w1span > (int64_t)INT_MAX || (int64_t)kLmBV * w2_row_stride * 2 > (int64_t)INT_MAX) return SPEC_EINVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char *ws = (char *)workspace;
+
+    Ctx c = {};
+    c.target = draft_logits;
+    c.draft = draft_logits;
+    c.tbs = q_batch_stride;
+    c.trs = q_row_stride;
+    c.dbs = q_batch_stride;
+    c.drs = q_row_stride;
+    c.K = K - 1;                         // q has K rows per sequence, tokens [b, K]
+    c.V = V;
+    c.nseg = L.nseg;
+    c.nres = 0;
+    c.rps = K;
+    c.row_lo = 0;
+    c.rpl = K;
+    c.temps = temperatures;
+    c.seeds = seeds;
+    c.tok = tokens;
+    c.part = (Partial *)(ws + L.part_off);
+    c.plan = (DrawPlan *)(ws + L.plan_off);
+    c.rmass = (double *)(ws + L.part_off);   // unused: no residual draws here
+    c.shard_id = -1;
+
+    LmArgs la = {};
+    la.hidden = (const uint16_t *)w1;
+    la.hrs = w1_row_stride;
+    la.hspan_bytes = (uint32_t)(w1span * 2);
+    la.weight = (const uint16_t *)w2;
+    la.wrs = w2_row_stride;
+    la.b = b;
+    la.K1 = 1;
+    la.V = V;
+    la.D = r;
+    la.M = b;
+    la.temps = temperatures;
+    la.K = K - 1;
+    la.logits = draft_logits;
+    la.lbs = q_batch_stride;
+    la.lrs = q_row_stride;
+    la.tpart = (Partial *)(ws + L.tpart_off);
+    la.ntiles = L.ntiles;
+    la.tiles_h = L.tiles_h;
+    la.store_all = 1;
+    la.base = base;
+    la.bbs = base_batch_stride;
+    la.brs = base_row_stride;
+    la.base_vec = (uintptr_t)base % 16 == 0 && base_row_stride % 4 == 0 && base_batch_stride % 4 == 0;
+    const unsigned grid_gemm = (unsigned)(L.ntiles * L.tiles_h);
+    const unsigned grid_merge = (unsigned)(((int64_t)b * L.nseg + kBlock - 1) / kBlock);
+    stage_mark(0, st);
+    for (int i = 0; i < K; ++i) {
+        const int32_t *prev = i == 0 ? anchors : tokens + (i - 1);
+        const int64_t pstride = i == 0 ? 1 : K;
+        la.gather_tok = prev;
+        la.gather_stride = pstride;
+        la.row_i0 = i;
+        hipLaunchKernelGGL(lm_head_kernel, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        hipLaunchKernelGGL(tile_merge_kernel, dim3(grid_merge), dim3(kBlock), 0, st, c, (const Partial *)la.tpart,
+                           L.ntiles, 1, b, i);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        hipLaunchKernelGGL(draft_pick_kernel, dim3((unsigned)b), dim3(kWave), 0, st, c, i, prev, pstride);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        hipLaunchKernelGGL((draw_kernel<SPEC_F32, true>), dim3((unsigned)b), dim3(kBlock), 0, st, c);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    }
+    stage_mark(1, st);
+    if (want_conf) {
+        hipLaunchKernelGGL(confidence_kernel, dim3((unsigned)b), dim3(kWave), 0, st, (const uint16_t *)hidden,
+                           h_batch_stride, h_row_stride, D, (const uint16_t *)w1, w1_row_stride, r,
+                           (const uint16_t *)conf_w, conf_b, anchors, (const int32_t *)tokens, K, V, threshold,
+                           confidence, lengths);
+        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+    }
+    stage_mark(2, st);
+    return SPEC_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,164 @@
+"""GPU parity of the draft-side Markov block decode against the oracle.
+
+The corrected logits q_i = L_i + W2 W1[x_{i-1}] are formed on the matrix
+cores in float32 (bf16 products exact, sums in any order), so they differ
+from the oracle's float64 definition by at most
+    tol(v) = gamma_{r} * sum_j |W1[x_{i-1}, j] W2[v, j]| + 2^-23 * |q(v)|
+(the float32 summation bound, plus the rounding of the sum and of adding
+the base logit).  Positions are compared in order; tokens must be equal,
+except where the oracle sits within that perturbation of its decision (an
+argmax within tol of the runner-up, or a draw within the perturbed CDF's
+reach), which is counted and ends the comparison of that sequence (the
+next positions condition on a different token).  Confidences agree to
+1e-6 and the draft lengths exactly, except at a confidence within 1e-6 of
+the threshold.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.markov as OM
+import workloads as W
+from parity import Report, seeds_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import lossless_draft_verification_amd  # noqa: F401
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _run(case: W.MarkovCase, threshold: float, anchors=None, temps=None):
+    import lossless_draft_verification_amd as L
+    anchors = case.anchors if anchors is None else anchors
+    temps = case.temps if temps is None else temps
+    r = L.markov_block_decode(torch.from_numpy(case.base).cuda(), torch.from_numpy(anchors).cuda(),
+                              _bf16_dev(case.w1), _bf16_dev(case.w2),
+                              torch.from_numpy(np.ascontiguousarray(temps, np.float64)).cuda(),
+                              seeds_to_device(case.seeds), hidden=_bf16_dev(case.hidden),
+                              conf_w=_bf16_dev(case.conf_w), conf_b=case.conf_b, threshold=threshold)
+    torch.cuda.synchronize()
+    return (r.tokens.cpu().numpy(), r.logits.cpu().numpy(), r.confidence.cpu().numpy(),
+            r.lengths.cpu().numpy())
+
+
+def _compare(case: W.MarkovCase, gpu, res, threshold, name) -> Report:
+    tok_g, q_g, conf_g, len_g = gpu
+    tok_o, q_o = res["tokens"], res["logits64"]
+    w1f = W.bf16_to_f32(case.w1).astype(np.float64)
+    w2a = np.abs(W.bf16_to_f32(case.w2).astype(np.float64))
+    g_r = OM_gamma(case.r)
+    rep = Report()
+    max_ratio = 0.0
+    for s in range(case.b):
+        rep.sequences += 1
+        T = float(case.temps[s])
+        if T == 0.0:
+            rep.greedy_sequences += 1
+        else:
+            rep.sampling_sequences += 1
+        diverged = False
+        for i in range(case.K):
+            prev = case.anchors[s] if i == 0 else tok_o[s, i - 1]
+            tol = g_r * (np.abs(w1f[prev]) @ w2a.T) + 2.0 ** -23 * np.abs(q_o[s, i])
+            err = np.abs(q_g[s, i].astype(np.float64) - q_o[s, i])
+            max_ratio = max(max_ratio, float((err / tol).max()))
+            if not (err <= tol).all():
+                rep.failures.append(dict(case=name, seq=s, pos=i, what="corrected logits",
+                                         worst=float((err / tol).max())))
+                diverged = True
+                break
+            if abs(conf_g[s, i] - res["confidence"][s, i]) > 1e-6:
+                rep.failures.append(dict(case=name, seq=s, pos=i, what="confidence",
+                                         gpu=float(conf_g[s, i]), oracle=float(res["confidence"][s, i])))
+            if tok_g[s, i] == tok_o[s, i]:
+                continue
+            yg, yo = int(tok_g[s, i]), int(tok_o[s, i])
+            z = q_o[s, i]
+            if T == 0.0:
+                ok = 0 <= yg < case.V and z[yg] + tol[yg] >= z[yo] - tol[yo]
+            else:
+                zz = np.ascontiguousarray(res["logits"][s, i])[None, None, :]
+                F = oracle.draw_cdf(zz, np.zeros((1, 0, case.V), np.float32), T, 0, 0, False)
+                u = oracle.uniform(int(case.seeds[s]), s, i, OM.TAG_DRAFT)
+                t = u * F[-1]
+                band = 2.0 * np.expm1(2.0 * tol.max() / T) * F[-1] + 1e-6 * F[-1]
+                margin = (F[yg - 1] - t) if yg > yo else (t - F[yg])
+                ok = 0 <= yg < case.V and margin <= band
+            if ok:
+                rep.draw_near_tie_mismatch += 1
+            else:
+                rep.failures.append(dict(case=name, seq=s, pos=i, what="token", gpu=yg, oracle=yo))
+            diverged = True
+            break
+        if not diverged:
+            rep.exact_sequences += 1
+            if threshold > 0.0 and len_g[s] != res["lengths"][s]:
+                k = int(min(len_g[s], res["lengths"][s]))
+                if not abs(res["confidence"][s, k] - threshold) < 1e-6:
+                    rep.failures.append(dict(case=name, seq=s, what="length", gpu=int(len_g[s]),
+                                             oracle=int(res["lengths"][s])))
+    rep.max_prob_rel_err = max_ratio      # here: the largest logit error as a fraction of its bound
+    return rep
+
+
+def OM_gamma(n: int) -> float:
+    u = 2.0 ** -24
+    return (n + 1) * u / (1.0 - (n + 1) * u)
+
+
+def _check(rep: Report, name: str, max_near_tie_frac: float = 0.02):
+    rep.save(name)
+    assert not rep.failures, rep.failures[:3]
+    ties = rep.accept_near_tie_mismatch + rep.draw_near_tie_mismatch
+    assert ties <= max(1, max_near_tie_frac * max(rep.sequences, 1)), rep
+
+
+MARKOV_CASES = [
+    # name, b, K, V, r, D, threshold
+    ("small_ragged_vocab", 12, 5, 5000, 64, 32, 0.5),
+    ("rank256", 40, 7, 20011, 256, 128, 0.6),
+    ("two_row_tiles", 300, 3, 3000, 128, 16, 0.0),
+]
+
+
+@pytest.mark.parametrize("spec", MARKOV_CASES, ids=[c[0] for c in MARKOV_CASES])
+def test_markov_block_decode(spec):
+    name, b, K, V, r, D, thr = spec
+    rule = np.array([W.GREEDY, W.SAMPLING] * (b // 2) + [W.SAMPLING] * (b % 2))
+    case = W.make_markov_case(name, b=b, K=K, V=V, r=r, D=D, rule=rule, T=0.8, seed=61 + b)
+    gpu = _run(case, thr)
+    res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
+                          conf_w=case.conf_w, conf_b=case.conf_b, threshold=thr)
+    _check(_compare(case, gpu, res, thr, f"markov_{name}"), f"markov_{name}")
+
+
+def test_markov_invalid_inputs():
+    """An invalid temperature or anchor gives -1 tokens for that sequence only."""
+    case = W.make_markov_case("bad", b=6, K=3, V=2000, r=64, D=8, rule=W.GREEDY, seed=66)
+    temps = case.temps.copy()
+    temps[1] = -1.0
+    anchors = case.anchors.copy()
+    anchors[3] = case.V + 5
+    tok = _run(case, 0.0, anchors=anchors, temps=temps)[0]
+    assert (tok[1] == -1).all() and (tok[3] == -1).all()
+    ok = [0, 2, 4, 5]
+    res = OM.block_decode(case.base[ok], anchors[ok], case.w1, case.w2, temps[ok], case.seeds[ok])
+    assert (tok[ok] == res["tokens"]).all()
+
+
+def test_markov_full_size():
+    """b=128, K=7, V=262144, r=256, D=3840; rows 0..63 greedy, 64..127 sampled."""
+    case = W.markov_config()
+    gpu = _run(case, 0.6)
+    res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
+                          conf_w=case.conf_w, conf_b=case.conf_b, threshold=0.6)
+    _check(_compare(case, gpu, res, 0.6, "markov_full"), "markov_full")

@@ -9,8 +9,8 @@
 // draft block [K, V] with K draft tokens.  Each sequence follows the greedy
 // rule (temperature 0) or the speculative-sampling rule (temperature T > 0).
 //
-// Kernels (HBM-bound streaming reductions; no MFMA -- nothing here is a dense
-// contraction):
+// Verify kernels (HBM-bound streaming reductions; no MFMA -- nothing in the
+// verify itself is a dense contraction):
 //   row_pass       one single-wave workgroup per 16 KiB segment of a logit
 //                  row: 16 coalesced nontemporal 16-byte loads per lane,
 //                  then per lane either max + first argmax (greedy rows) or
@@ -29,6 +29,11 @@
 //                  the segment masses, re-read of the one segment holding t
 //                  into registers, block scan in double, inverse-CDF search.
 //
+// The fused verify (lm_head_fused.inc) and the draft-side Markov decode
+// (markov_draft.inc) add the one dense contraction on the path, the lm_head /
+// Markov-table GEMM, on the matrix cores; the vocabulary-sharded verify
+// (vocab_sharded.inc) runs the verify kernels per shard.
+//
 // Every merge and scan runs in a fixed order with no floating-point atomics,
 // so two calls on the same bytes give the same bits.  Kernel boundaries are
 // the only cross-workgroup synchronisation: a device-scope release fence per
@@ -41,6 +46,8 @@
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "specverify.h"
 
@@ -1056,7 +1063,8 @@ template <bool VEC>
 int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream_t st) {
     const Layout &L = F.L;
     stage_mark(0, st);
-    hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(F.ntiles * F.tiles_h)), dim3(kLmThreads), 0, st, la);
+    hipLaunchKernelGGL(lm_head_kernel<kEpiVerify>, dim3((unsigned)(F.ntiles * F.tiles_h)), dim3(kLmThreads), 0, st,
+                       la);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(1, st);
     const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg;
@@ -1283,7 +1291,6 @@ int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t 
     la.tpart = (Partial *)(ws + F.tpart_off);
     la.ntiles = F.ntiles;
     la.tiles_h = F.tiles_h;
-    la.write_all = 0;
     Ctx c = {};
     c.target = logits;
     c.draft = draft;
@@ -1352,8 +1359,8 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, cons
     la.lrs = 0;
     la.ntiles = (int)ntiles;
     la.tiles_h = (int)th;
-    la.write_all = 1;
-    hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(ntiles * th)), dim3(kLmThreads), 0, (hipStream_t)hip_stream, la);
+    hipLaunchKernelGGL(lm_head_kernel<kEpiLogits>, dim3((unsigned)(ntiles * th)), dim3(kLmThreads), 0,
+                       (hipStream_t)hip_stream, la);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
@@ -1507,7 +1514,6 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     la.tpart = (Partial *)(ws + L.tpart_off);
     la.ntiles = L.ntiles;
     la.tiles_h = L.tiles_h;
-    la.store_all = 1;
     la.base = base;
     la.bbs = base_batch_stride;
     la.brs = base_row_stride;
@@ -1521,7 +1527,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         la.gather_tok = prev;
         la.gather_stride = pstride;
         la.row_i0 = i;
-        hipLaunchKernelGGL(lm_head_kernel, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
+        hipLaunchKernelGGL(lm_head_kernel<kEpiMarkov>, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(tile_merge_kernel, dim3(grid_merge), dim3(kBlock), 0, st, c, (const Partial *)la.tpart,
                            L.ntiles, 1, b, i);

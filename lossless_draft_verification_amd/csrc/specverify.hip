@@ -1495,6 +1495,9 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     c.rmass = (double *)(ws + L.part_off);   // unused: no residual draws here
     c.shard_id = -1;
 
+    // the correction rows W2 u_i: the lm_head kernel storing every row (no
+    // softcap), its hidden rows gathered from W1 by the previous token
+    float *corr = (float *)(ws + L.corr_off);
     LmArgs la = {};
     la.hidden = (const uint16_t *)w1;
     la.hrs = w1_row_stride;
@@ -1506,31 +1509,29 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     la.V = V;
     la.D = r;
     la.M = b;
-    la.temps = temperatures;
-    la.K = K - 1;
-    la.logits = draft_logits;
-    la.lbs = q_batch_stride;
-    la.lrs = q_row_stride;
-    la.tpart = (Partial *)(ws + L.tpart_off);
+    la.logits = corr;
+    la.lbs = L.crs;
+    la.lrs = 0;
     la.ntiles = L.ntiles;
     la.tiles_h = L.tiles_h;
-    la.base = base;
-    la.bbs = base_batch_stride;
-    la.brs = base_row_stride;
-    la.base_vec = (uintptr_t)base % 16 == 0 && base_row_stride % 4 == 0 && base_batch_stride % 4 == 0;
+    const bool base_vec = (uintptr_t)base % 16 == 0 && base_row_stride % 4 == 0 && base_batch_stride % 4 == 0;
     const unsigned grid_gemm = (unsigned)(L.ntiles * L.tiles_h);
-    const unsigned grid_merge = (unsigned)(((int64_t)b * L.nseg + kBlock - 1) / kBlock);
+    const int64_t grid_rows = (int64_t)b * L.nseg;
+    if (grid_rows > INT_MAX) return SPEC_EINVAL;
     stage_mark(0, st);
     for (int i = 0; i < K; ++i) {
         const int32_t *prev = i == 0 ? anchors : tokens + (i - 1);
         const int64_t pstride = i == 0 ? 1 : K;
         la.gather_tok = prev;
         la.gather_stride = pstride;
-        la.row_i0 = i;
-        hipLaunchKernelGGL(lm_head_kernel<kEpiMarkov>, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
+        hipLaunchKernelGGL(lm_head_kernel<kEpiLogits>, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(tile_merge_kernel, dim3(grid_merge), dim3(kBlock), 0, st, c, (const Partial *)la.tpart,
-                           L.ntiles, 1, b, i);
+        if (base_vec)
+            hipLaunchKernelGGL(markov_row_kernel<true>, dim3((unsigned)grid_rows), dim3(kWave), 0, st, c,
+                               (const float *)corr, L.crs, base, base_batch_stride, base_row_stride, i);
+        else
+            hipLaunchKernelGGL(markov_row_kernel<false>, dim3((unsigned)grid_rows), dim3(kWave), 0, st, c,
+                               (const float *)corr, L.crs, base, base_batch_stride, base_row_stride, i);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(draft_pick_kernel, dim3((unsigned)b), dim3(kWave), 0, st, c, i, prev, pstride);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
@@ -1539,11 +1540,17 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     }
     stage_mark(1, st);
     if (want_conf) {
-        hipLaunchKernelGGL(confidence_kernel, dim3((unsigned)b), dim3(kWave), 0, st, (const uint16_t *)hidden,
+        const int vec = (uintptr_t)hidden % 16 == 0 && h_row_stride % 8 == 0 && h_batch_stride % 8 == 0 &&
+                        (uintptr_t)conf_w % 16 == 0;
+        hipLaunchKernelGGL(confidence_kernel, dim3((unsigned)(b * K)), dim3(kWave), 0, st, (const uint16_t *)hidden,
                            h_batch_stride, h_row_stride, D, (const uint16_t *)w1, w1_row_stride, r,
-                           (const uint16_t *)conf_w, conf_b, anchors, (const int32_t *)tokens, K, V, threshold,
-                           confidence, lengths);
+                           (const uint16_t *)conf_w, conf_b, anchors, (const int32_t *)tokens, K, V, vec, confidence);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        if (lengths) {
+            hipLaunchKernelGGL(draft_length_kernel, dim3((unsigned)((b + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                               (const float *)confidence, b, K, threshold, lengths);
+            if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+        }
     }
     stage_mark(2, st);
     return SPEC_OK;

@@ -54,8 +54,14 @@ def cpu_model() -> str:
 
 
 def source_digest() -> str:
-    with open(os.path.join(ROOT, "lossless_draft_verification_amd", "csrc", "specverify.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over every kernel source file (sorted by name)."""
+    d = os.path.join(ROOT, "lossless_draft_verification_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".inc")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
@@ -189,6 +195,56 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
         json.dump(traffic, f, indent=1)
     print("\n".join(lines))
     return 0
+
+
+TRACE_SUMMARIES = [
+    # (trace dir, -o prefix, profile file, title, workload text, bench arguments)
+    ("prof_fused", "fused", "lm_head_fused_verify_b128_V262144_D3840.md",
+     "Kernel durations: fused lm_head + verify",
+     "b=128, K=7, V=262144, D=3840, bf16 hidden states and lm_head weight, softcap 30, float32 drafter "
+     "logits; sequences 0..63 greedy, 64..127 sampled at T=0.8; one spec_fused_mixed_accept call per step.",
+     "--fused --steps 50 --warmup 5 --no-cpu-baseline --no-reference"),
+    ("prof_markov", "markov", "markov_block_decode_b128_V262144_r256.md",
+     "Kernel durations: draft-side Markov block decode",
+     "b=128, K=7, V=262144, r=256, D=3840; float32 base logits, bf16 Markov tables, confidence head; "
+     "sequences 0..63 greedy, 64..127 sampled at T=0.8; one spec_markov_block_decode call per step "
+     "(7 positions: GEMM, row pass, pick and draw each).",
+     "--markov --steps 30 --warmup 3 --no-cpu-baseline"),
+    ("prof_sharded", "sharded", "verify_c5_vocab_sharded8.md",
+     "Kernel durations: vocabulary-sharded verify, 8 shards",
+     "workload c5 (b=128, K=7, V=262144, bf16, 64 greedy + 64 sampled) with the vocabulary in 8 shards of "
+     "32768 columns, one spec_sharded_mixed_accept call per step.",
+     "--sharded 8 --steps 200 --warmup 200 --no-cpu-baseline --no-reference"),
+]
+
+
+def summarize_traces(rdir: str) -> None:
+    """profiles/*.md summaries of the kernel traces of the fused, Markov and
+    sharded paths (whichever are present under rdir)."""
+    import csv
+    digest = source_digest()
+    for sub, prefix, fname, title, workload, bargs in TRACE_SUMMARIES:
+        path = os.path.join(rdir, sub, f"{prefix}_kernel_stats.csv")
+        if not os.path.exists(path):
+            continue
+        rows = list(csv.DictReader(open(path)))
+        lines = [f"# {title}", "", workload, f"Kernel source sha256[:16] = `{digest}`.", "",
+                 "Command (run from /tmp, repository at $R, rocprofv3 output under $OUT):", "",
+                 f"    rocprofv3 --kernel-trace --stats -d $OUT/{sub} -o {prefix} --output-format csv \\",
+                 f"        -- python3 $R/bench.py {bargs}",
+                 "    python bench.py --summarize-rocprof $OUT            # writes this file", "",
+                 "## rocprofv3 --stats (kernel stats), all launches of the run", "",
+                 "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            name = r["Name"]
+            if "anonymous namespace" not in name:
+                continue
+            short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+            lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote profiles/{fname}")
 
 
 def copy_calibration(nbytes: int) -> int:
@@ -526,6 +582,7 @@ def main() -> int:
                     help="write profiles/ summaries from rocprofv3 CSVs under DIR and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
+        summarize_traces(args.summarize_rocprof)
         return summarize_rocprof(args.summarize_rocprof)
     if (args.ragged or args.sharded) and args.step != "mixed":
         print("--ragged and --sharded need --step mixed", file=sys.stderr)

@@ -1063,8 +1063,7 @@ template <bool VEC>
 int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream_t st) {
     const Layout &L = F.L;
     stage_mark(0, st);
-    hipLaunchKernelGGL(lm_head_kernel<kEpiVerify>, dim3((unsigned)(F.ntiles * F.tiles_h)), dim3(kLmThreads), 0, st,
-                       la);
+    launch_lm_head<kEpiVerify>(la, (unsigned)(F.ntiles * F.tiles_h), st);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(1, st);
     const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg;
@@ -1359,8 +1358,7 @@ int spec_lm_head_logits(const void *hidden, int64_t h_row_stride, int rows, cons
     la.lrs = 0;
     la.ntiles = (int)ntiles;
     la.tiles_h = (int)th;
-    hipLaunchKernelGGL(lm_head_kernel<kEpiLogits>, dim3((unsigned)(ntiles * th)), dim3(kLmThreads), 0,
-                       (hipStream_t)hip_stream, la);
+    launch_lm_head<kEpiLogits>(la, (unsigned)(ntiles * th), (hipStream_t)hip_stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
@@ -1524,7 +1522,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         const int64_t pstride = i == 0 ? 1 : K;
         la.gather_tok = prev;
         la.gather_stride = pstride;
-        hipLaunchKernelGGL(lm_head_kernel<kEpiLogits>, dim3(grid_gemm), dim3(kLmThreads), 0, st, la);
+        launch_lm_head<kEpiLogits>(la, grid_gemm, st);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         if (base_vec)
             hipLaunchKernelGGL(markov_row_kernel<true>, dim3((unsigned)grid_rows), dim3(kWave), 0, st, c,

@@ -428,7 +428,7 @@ def main_fused(args) -> int:
         "config": {"workload": "fused: " + W.FUSED_TEXT, "b": b, "K": K, "V": V, "D": D, "softcap": cap,
                    "greedy_sequences": int((case.temps == 0.0).sum()), "sampling_sequences": bs,
                    "step": "one spec_fused_mixed_accept call", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "lm_head_kernel", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "lm_head_dl_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None, "algorithmic_flops_per_launch": gemm_flops,
                      "avg_launch_ms": stage["lm_head_gemm"]},
@@ -542,7 +542,7 @@ def main_markov(args) -> int:
         "config": {"workload": "markov: " + W.MARKOV_TEXT, "b": b, "K": K, "V": V, "r": r, "D": D,
                    "confidence_threshold": 0.6, "step": "one spec_markov_block_decode call",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "position loop (lm_head_kernel in gather mode + merge + pick + draw)",
+        "roofline": {"bound": "hbm", "kernel": "position loop (lm_head_dl_kernel in gather mode + merge + pick + draw)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms},
         "stage_ms": {"position_loop": loop_ms, "confidence": conf_ms},

@@ -1066,9 +1066,9 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
     launch_lm_head<kEpiVerify>(la, (unsigned)(F.ntiles * F.tiles_h), st);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(1, st);
-    const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg;
+    const int64_t nmerge = (int64_t)b * (c.K + 1) * L.nseg * kLmTilesPerSeg;
     hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c,
-                       (const Partial *)la.tpart, F.ntiles, c.K + 1, b, 0);
+                       (const Partial *)la.tpart, F.ntiles, c.K + 1, b, 0, kLmTilesPerSeg);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(2, st);
     // draft rows only (partial rows K+1 .. 2K)
@@ -1467,7 +1467,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     if (!bf16_operand_ok(w1, w1_row_stride, r) || !bf16_operand_ok(w2, w2_row_stride, r)) return SPEC_EALIGN;
     if (want_conf && ((uintptr_t)hidden % 2 || (uintptr_t)conf_w % 2)) return SPEC_EALIGN;
     const int64_t w1span = (int64_t)(V - 1) * w1_row_stride + r;
-    if (w1span > (int64_t)INT_MAX || (int64_t)kLmBV * w2_row_stride * 2 > (int64_t)INT_MAX) return SPEC_EINVAL;
+    if (w1span > (int64_t)INT_MAX || (int64_t)MqS::kBV * w2_row_stride * 2 > (int64_t)INT_MAX) return SPEC_EINVAL;
     hipStream_t st = (hipStream_t)hip_stream;
     char *ws = (char *)workspace;
 
@@ -1493,43 +1493,40 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     c.rmass = (double *)(ws + L.part_off);   // unused: no residual draws here
     c.shard_id = -1;
 
-    // the correction rows W2 u_i: the lm_head kernel storing every row (no
-    // softcap), its hidden rows gathered from W1 by the previous token
-    float *corr = (float *)(ws + L.corr_off);
-    LmArgs la = {};
-    la.hidden = (const uint16_t *)w1;
-    la.hrs = w1_row_stride;
-    la.hspan_bytes = (uint32_t)(w1span * 2);
-    la.weight = (const uint16_t *)w2;
-    la.wrs = w2_row_stride;
-    la.b = b;
-    la.K1 = 1;
-    la.V = V;
-    la.D = r;
-    la.M = b;
-    la.logits = corr;
-    la.lbs = L.crs;
-    la.lrs = 0;
-    la.ntiles = L.ntiles;
-    la.tiles_h = L.tiles_h;
-    const bool base_vec = (uintptr_t)base % 16 == 0 && base_row_stride % 4 == 0 && base_batch_stride % 4 == 0;
-    const unsigned grid_gemm = (unsigned)(L.ntiles * L.tiles_h);
-    const int64_t grid_rows = (int64_t)b * L.nseg;
-    if (grid_rows > INT_MAX) return SPEC_EINVAL;
+    MqArgs ma = {};
+    ma.w1 = (const uint16_t *)w1;
+    ma.w1rs = w1_row_stride;
+    ma.w1span = (uint32_t)(w1span * 2);
+    ma.w2 = (const uint16_t *)w2;
+    ma.w2rs = w2_row_stride;
+    ma.base = base;
+    ma.bbs = base_batch_stride;
+    ma.brs = base_row_stride;
+    ma.q = draft_logits;
+    ma.qbs = q_batch_stride;
+    ma.qrs = q_row_stride;
+    ma.temps = temperatures;
+    ma.b = b;
+    ma.V = V;
+    ma.r = r;
+    ma.ntiles = L.ntiles;
+    ma.tiles_h = L.tiles_h;
+    ma.tpart = (Partial *)(ws + L.tpart_off);
+    const unsigned grid_q = (unsigned)(L.ntiles * L.tiles_h);
+    constexpr int kMqTilesPerSeg = (int)(seg_elems(SPEC_F32) / MqS::kBV);
+    const int64_t nmerge = (int64_t)b * L.nseg * kMqTilesPerSeg;
     stage_mark(0, st);
     for (int i = 0; i < K; ++i) {
         const int32_t *prev = i == 0 ? anchors : tokens + (i - 1);
         const int64_t pstride = i == 0 ? 1 : K;
-        la.gather_tok = prev;
-        la.gather_stride = pstride;
-        launch_lm_head<kEpiLogits>(la, grid_gemm, st);
+        ma.prev = prev;
+        ma.pstride = pstride;
+        ma.step = i;
+        hipLaunchKernelGGL((markov_q_kernel<MqS::kBV, MqS::kBH, MqS::kNW, MqS::kNST>), dim3(grid_q),
+                           dim3(MqS::kThreads), 0, st, ma);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        if (base_vec)
-            hipLaunchKernelGGL(markov_row_kernel<true>, dim3((unsigned)grid_rows), dim3(kWave), 0, st, c,
-                               (const float *)corr, L.crs, base, base_batch_stride, base_row_stride, i);
-        else
-            hipLaunchKernelGGL(markov_row_kernel<false>, dim3((unsigned)grid_rows), dim3(kWave), 0, st, c,
-                               (const float *)corr, L.crs, base, base_batch_stride, base_row_stride, i);
+        hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                           c, (const Partial *)ma.tpart, L.ntiles, 1, b, i, kMqTilesPerSeg);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(draft_pick_kernel, dim3((unsigned)b), dim3(kWave), 0, st, c, i, prev, pstride);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;

@@ -295,8 +295,9 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
  *                   strides multiples of 4
  *   confidence      float [b, K] out or NULL; lengths int32 [b] out or NULL
  *   workspace       spec_markov_workspace_bytes(b, K, V, r) bytes, 256-byte aligned
- * Four kernels per position (correction GEMM, streaming row pass adding the
- * base logits, pick, draw), then the confidence and length kernels.
+ * Four kernels per position (the correction on the matrix cores with the
+ * base logits added, q_i stored and per-tile records; the merge of the tile
+ * records; pick; draw), then the confidence and length kernels.
  */
 size_t spec_markov_workspace_bytes(int b, int K, int V, int r);
 

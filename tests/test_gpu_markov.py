@@ -127,6 +127,7 @@ MARKOV_CASES = [
     ("small_ragged_vocab", 12, 5, 5000, 64, 32, 0.5),
     ("rank256", 40, 7, 20011, 256, 128, 0.6),
     ("two_row_tiles", 300, 3, 3000, 128, 16, 0.0),
+    ("rank320", 20, 4, 3001, 320, 16, 0.5),
 ]
 
 

@@ -897,16 +897,20 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
 // workgroups stream measurably faster on this part than 4-wave ones: a wave
 // starts as soon as one wave's resources free up.)
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
-    const int lane = threadIdx.x;
-    const int row = blockIdx.x / c.nseg;
-    const int seg = blockIdx.x - row * c.nseg;
+__device__ inline void row_pass_block(const Ctx &c, int blk, int lane) {
+    const int row = blk / c.nseg;
+    const int seg = blk - row * c.nseg;
     const int s = row / c.rpl, i = c.row_lo + (row - s * c.rpl);
     const double T = seq_temperature(c, s);
     const int Ks = seq_len(c, s);
     const int rule = seq_rule(c, T, Ks);
     if (rule == kRuleInvalid || (rule == kRuleGreedy && i > c.K) || !row_in_block(i, c.K, Ks)) return;
     row_wave<DT, VEC>(c, s, i, seg, lane, rule, T);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
+    row_pass_block<DT, VEC>(c, (int)blockIdx.x, (int)threadIdx.x);
 }
 
 // Scan of every sequence of the call: one 1024-thread block per sequence.
@@ -1435,8 +1439,13 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
     call.q_out = q_draft;
     call.am = target_argmax;
     hipStream_t st = (hipStream_t)hip_stream;
-    return dtype == SPEC_BF16 ? launch_sharded<SPEC_BF16>(cg, vec, call, b, S, ws, st)
-                              : launch_sharded<SPEC_F32>(cg, vec, call, b, S, ws, st);
+    bool all_vec = true;
+    for (int g = 0; g < G; ++g) all_vec = all_vec && vec[g];
+    if (dtype == SPEC_BF16)
+        return all_vec ? launch_sharded<SPEC_BF16, true>(cg, call, b, S, ws, st)
+                       : launch_sharded<SPEC_BF16, false>(cg, call, b, S, ws, st);
+    return all_vec ? launch_sharded<SPEC_F32, true>(cg, call, b, S, ws, st)
+                   : launch_sharded<SPEC_F32, false>(cg, call, b, S, ws, st);
 }
 
 size_t spec_markov_workspace_bytes(int b, int K, int V, int r) {

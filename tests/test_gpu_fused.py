@@ -138,3 +138,14 @@ def test_fused_full_size_sampled():
     # from ties (planted gain >= 10 over a background of N(0, 9))
     n = out[0]
     assert (n >= 0).all()
+
+
+def test_fused_deterministic_repeat():
+    """Two calls on the same inputs give the same bytes (every merge is in a
+    fixed order; there are no floating-point atomics)."""
+    b, K = 40, 5
+    rule = np.array([W.GREEDY, W.SAMPLING] * (b // 2))
+    case = W.make_fused_case("fdet", b=b, K=K, V=12000, D=256, softcap=30.0, rule=rule, T=0.9, seed=74)
+    a, c = _run_fused(case), _run_fused(case)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)

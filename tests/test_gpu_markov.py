@@ -163,3 +163,13 @@ def test_markov_full_size():
     res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
                           conf_w=case.conf_w, conf_b=case.conf_b, threshold=0.6)
     _check(_compare(case, gpu, res, 0.6, "markov_full"), "markov_full")
+
+
+def test_markov_deterministic_repeat():
+    """Two calls on the same inputs give the same tokens, logits, confidences
+    and lengths, bit for bit."""
+    case = W.make_markov_case("mdet", b=40, K=5, V=9000, r=128, D=32,
+                              rule=np.array([W.GREEDY, W.SAMPLING] * 20), T=0.9, seed=67)
+    a, c = _run(case, 0.5), _run(case, 0.5)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)

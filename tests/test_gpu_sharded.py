@@ -109,3 +109,14 @@ def test_sharded_workload_c5_eight_shards():
     ref = _run_unsharded(case, temps)
     for a, r in zip((out[0], out[1], out[4]), (ref[0], ref[1], ref[4])):
         np.testing.assert_array_equal(a, r)
+
+
+def test_sharded_deterministic_repeat():
+    """Two calls on the same shards give the same bytes."""
+    b, K = 20, 5
+    case = W.make_case("shard_det", b=b, K=K, V=12000, dtype="bf16", target_scale=2.5, draft_sigma=(0.2, 1.5),
+                       T=0.8, seed=93)
+    temps = np.where(np.arange(b) % 2 == 0, 0.0, 0.8)
+    a, c = _run(case, temps, [4000, 5000, 3000]), _run(case, temps, [4000, 5000, 3000])
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)

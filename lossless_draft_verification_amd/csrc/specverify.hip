@@ -1099,6 +1099,19 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
 #include "vocab_sharded.inc"
 #include "markov_draft.inc"
 
+// Compute units of the current device (0 if it cannot be read), read once
+// per device.
+int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
 bool bf16_operand_ok(const void *p, int64_t stride, int D) {
     return p && (uintptr_t)p % 16 == 0 && stride >= D && stride % 8 == 0;
 }
@@ -1522,17 +1535,71 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     ma.tiles_h = L.tiles_h;
     ma.tpart = (Partial *)(ws + L.tpart_off);
     const unsigned grid_q = (unsigned)(L.ntiles * L.tiles_h);
+    static_assert(kMsBV == MqS::kBV, "both position kernels write 128-entry tile records");
     constexpr int kMqTilesPerSeg = (int)(seg_elems(SPEC_F32) / MqS::kBV);
     const int64_t nmerge = (int64_t)b * L.nseg * kMqTilesPerSeg;
+
+    // Ranks up to 256 (multiples of 64) with 16-byte aligned base rows whose
+    // 128-sequence span fits a 31-bit offset: the persistent streaming kernel,
+    // one workgroup per CU.
+    static_assert(kMsMaxR == 256, "one streaming instance per r / 64 in 1..4");
+    const bool streaming = r <= kMsMaxR && (uintptr_t)base % 16 == 0 && base_batch_stride % 4 == 0 &&
+                           base_row_stride % 4 == 0 && (int64_t)(kMsBH - 1) * base_batch_stride * 4 + 128 < INT_MAX;
+    MsArgs sa = {};
+    unsigned grid_s = 0;
+    if (streaming) {
+        const int ncu = device_cu_count();
+        if (ncu < 1) return SPEC_ELAUNCH;
+        sa.w1 = ma.w1;
+        sa.w1rs = w1_row_stride;
+        sa.w2 = ma.w2;
+        sa.w2rs = w2_row_stride;
+        sa.base = base;
+        sa.bbs = base_batch_stride;
+        sa.brs = base_row_stride;
+        sa.base_end = (int64_t)(b - 1) * base_batch_stride + (int64_t)(K - 1) * base_row_stride + V;
+        sa.q = draft_logits;
+        sa.qbs = q_batch_stride;
+        sa.qrs = q_row_stride;
+        sa.temps = temperatures;
+        sa.b = b;
+        sa.V = V;
+        sa.r = r;
+        sa.ntiles = L.ntiles;
+        sa.P = min(L.ntiles, max(1, ncu / L.tiles_h));     // every workgroup gets at least one tile
+        const int stage = kMsChunkRows * r * 2 + kMsBaseB;    // a chunk's W2 rows and base logits
+        const int icp = stage / 1024 / kMsPW;                 // loads per chunk per producer wave
+        sa.ahead = min(63 / icp - 1, 15);                     // (ahead + 1) * icp loads in flight at most
+        sa.nst = sa.ahead + 2;
+        while (sa.nst * stage > kMsRingB) {
+            --sa.nst;
+            sa.ahead = sa.nst - 2;
+        }
+        sa.tpart = ma.tpart;
+        if ((int64_t)sa.P * L.tiles_h > INT_MAX) return SPEC_EINVAL;
+        grid_s = (unsigned)(sa.P * L.tiles_h);
+    }
     stage_mark(0, st);
     for (int i = 0; i < K; ++i) {
         const int32_t *prev = i == 0 ? anchors : tokens + (i - 1);
         const int64_t pstride = i == 0 ? 1 : K;
-        ma.prev = prev;
-        ma.pstride = pstride;
-        ma.step = i;
-        hipLaunchKernelGGL((markov_q_kernel<MqS::kBV, MqS::kBH, MqS::kNW, MqS::kNST>), dim3(grid_q),
-                           dim3(MqS::kThreads), 0, st, ma);
+        if (streaming) {
+            sa.prev = prev;
+            sa.pstride = pstride;
+            sa.step = i;
+            switch (r / 64) {
+            case 1: hipLaunchKernelGGL(markov_stream_kernel<2>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
+            case 2: hipLaunchKernelGGL(markov_stream_kernel<4>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
+            case 3: hipLaunchKernelGGL(markov_stream_kernel<6>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
+            default: hipLaunchKernelGGL(markov_stream_kernel<8>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
+            }
+        } else {
+            ma.prev = prev;
+            ma.pstride = pstride;
+            ma.step = i;
+            hipLaunchKernelGGL((markov_q_kernel<MqS::kBV, MqS::kBH, MqS::kNW, MqS::kNST>), dim3(grid_q),
+                               dim3(MqS::kThreads), 0, st, ma);
+        }
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                            c, (const Partial *)ma.tpart, L.ntiles, 1, b, i, kMqTilesPerSeg);

@@ -125,9 +125,12 @@ def _check(rep: Report, name: str, max_near_tie_frac: float = 0.02):
 MARKOV_CASES = [
     # name, b, K, V, r, D, threshold
     ("small_ragged_vocab", 12, 5, 5000, 64, 32, 0.5),
-    ("rank256", 40, 7, 20011, 256, 128, 0.6),
+    ("rank256", 40, 7, 20012, 256, 128, 0.6),
+    ("rank256_odd_vocab_tiled_kernel", 40, 7, 20011, 256, 128, 0.6),
     ("two_row_tiles", 300, 3, 3000, 128, 16, 0.0),
     ("rank320", 20, 4, 3001, 320, 16, 0.5),
+    ("rank192_two_seq_tiles", 130, 3, 4099, 192, 16, 0.5),
+    ("rank384_tiled_kernel", 16, 3, 2500, 384, 16, 0.5),
 ]
 
 

@@ -208,7 +208,7 @@ TRACE_SUMMARIES = [
      "Kernel durations: draft-side Markov block decode",
      "b=128, K=7, V=262144, r=256, D=3840; float32 base logits, bf16 Markov tables, confidence head; "
      "sequences 0..63 greedy, 64..127 sampled at T=0.8; one spec_markov_block_decode call per step "
-     "(7 positions: correction kernel, tile merge, pick and draw each).",
+     "(7 positions: the streaming correction kernel and the per-sequence select kernel each).",
      "--markov --steps 30 --warmup 3 --no-cpu-baseline"),
     ("prof_sharded", "sharded", "verify_c5_vocab_sharded8.md",
      "Kernel durations: vocabulary-sharded verify, 8 shards",
@@ -542,7 +542,7 @@ def main_markov(args) -> int:
         "config": {"workload": "markov: " + W.MARKOV_TEXT, "b": b, "K": K, "V": V, "r": r, "D": D,
                    "confidence_threshold": 0.6, "step": "one spec_markov_block_decode call",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "position loop (markov_q_kernel + tile_merge_kernel + draft_pick_kernel + draw_kernel, 7 positions)",
+        "roofline": {"bound": "hbm", "kernel": "position loop (markov_stream_kernel + draft_select_kernel, 7 positions)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms},
         "stage_ms": {"position_loop": loop_ms, "confidence": conf_ms},

@@ -1536,8 +1536,6 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     ma.tpart = (Partial *)(ws + L.tpart_off);
     const unsigned grid_q = (unsigned)(L.ntiles * L.tiles_h);
     static_assert(kMsBV == MqS::kBV, "both position kernels write 128-entry tile records");
-    constexpr int kMqTilesPerSeg = (int)(seg_elems(SPEC_F32) / MqS::kBV);
-    const int64_t nmerge = (int64_t)b * L.nseg * kMqTilesPerSeg;
 
     // Ranks up to 256 (multiples of 64) with 16-byte aligned base rows whose
     // 128-sequence span fits a 31-bit offset: the persistent streaming kernel,
@@ -1569,7 +1567,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         sa.P = min(L.ntiles, max(1, ncu / L.tiles_h));     // every workgroup gets at least one tile
         const int stage = kMsChunkRows * r * 2 + kMsBaseB;    // a chunk's W2 rows and base logits
         const int icp = stage / 1024 / kMsPW;                 // loads per chunk per producer wave
-        sa.ahead = min(63 / icp - 1, 15);                     // (ahead + 1) * icp loads in flight at most
+        sa.ahead = min((63 - kMsZp) / icp - 1, 15);           // (ahead + 1) * icp loads and kMsZp stores in flight
         sa.nst = sa.ahead + 2;
         while (sa.nst * stage > kMsRingB) {
             --sa.nst;
@@ -1601,12 +1599,8 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
                                dim3(MqS::kThreads), 0, st, ma);
         }
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(tile_merge_kernel, dim3((unsigned)((nmerge + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
-                           c, (const Partial *)ma.tpart, L.ntiles, 1, b, i, kMqTilesPerSeg);
-        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(draft_pick_kernel, dim3((unsigned)b), dim3(kWave), 0, st, c, i, prev, pstride);
-        if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        hipLaunchKernelGGL((draw_kernel<SPEC_F32, true>), dim3((unsigned)b), dim3(kBlock), 0, st, c);
+        hipLaunchKernelGGL(draft_select_kernel, dim3((unsigned)b), dim3(kBlock), 0, st, c, i,
+                           (const Partial *)ma.tpart, L.ntiles, prev, pstride);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     }
     stage_mark(1, st);

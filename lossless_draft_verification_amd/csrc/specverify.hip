@@ -1541,6 +1541,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     // 128-sequence span fits a 31-bit offset: the persistent streaming kernel,
     // one workgroup per CU.
     static_assert(kMsMaxR == 256, "one streaming instance per r / 64 in 1..4");
+    uint16_t *ubuf = (uint16_t *)(ws + L.ubuf_off);        // [b, r]: W1 rows of the last drawn tokens
     const bool streaming = r <= kMsMaxR && (uintptr_t)base % 16 == 0 && base_batch_stride % 4 == 0 &&
                            base_row_stride % 4 == 0 && (int64_t)(kMsBH - 1) * base_batch_stride * 4 + 128 < INT_MAX;
     MsArgs sa = {};
@@ -1584,6 +1585,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         if (streaming) {
             sa.prev = prev;
             sa.pstride = pstride;
+            sa.ubuf = i == 0 ? nullptr : ubuf;          // from position 1 on, the rows the select copied
             sa.step = i;
             switch (r / 64) {
             case 1: hipLaunchKernelGGL(markov_stream_kernel<2>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
@@ -1600,7 +1602,8 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         }
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(draft_select_kernel, dim3((unsigned)b), dim3(kBlock), 0, st, c, i,
-                           (const Partial *)ma.tpart, L.ntiles, prev, pstride);
+                           (const Partial *)ma.tpart, L.ntiles, prev, pstride, (const uint16_t *)w1, w1_row_stride, r,
+                           streaming && i + 1 < K ? ubuf : nullptr);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     }
     stage_mark(1, st);

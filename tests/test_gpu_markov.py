@@ -131,6 +131,9 @@ MARKOV_CASES = [
     ("rank320", 20, 4, 3001, 320, 16, 0.5),
     ("rank192_two_seq_tiles", 130, 3, 4099, 192, 16, 0.5),
     ("rank384_tiled_kernel", 16, 3, 2500, 384, 16, 0.5),
+    ("vocab4", 3, 2, 4, 64, 8, 0.5),
+    ("one_tile_and_a_bit", 5, 3, 132, 128, 8, 0.5),
+    ("single_sequence", 1, 7, 4096, 256, 16, 0.5),
 ]
 
 

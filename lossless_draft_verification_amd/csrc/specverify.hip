@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "specverify.h"
@@ -1100,15 +1101,19 @@ int launch_fused(Ctx c, const LmArgs &la, int b, const FusedLayout &F, hipStream
 #include "markov_draft.inc"
 
 // Compute units of the current device (0 if it cannot be read), read once
-// per device.
+// per device; callers on several host threads may race to fill the cache
+// with the same value.
 int device_cu_count() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) cached[dev] = n;
+    if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

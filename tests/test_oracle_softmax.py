@@ -57,3 +57,36 @@ def test_reported_probabilities_match_scipy(orc):
             assert res["p_draft"][s, i] == pytest.approx(p, rel=1e-12)
             assert res["q_draft"][s, i] == pytest.approx(q, rel=1e-12)
             assert res["r"][s, i] == pytest.approx(p / q, rel=1e-11)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("residual", [False, True])
+def test_draw_cdf_matches_scipy(orc, dtype, residual):
+    """The running sums the draw inverts: of softmax(p_n / T) (target mode) or
+    of max(0, softmax(p_n / T) - softmax(q_n / T)) (residual mode), against
+    scipy's softmax summed by numpy."""
+    rng = np.random.default_rng(29)
+    b, K, V, T = 2, 3, 3000, 0.8
+    target = _rows(rng, b * (K + 1), V, dtype, 2.5).reshape(b, K + 1, V)
+    draft = _rows(rng, b * K, V, dtype, 2.5).reshape(b, K, V)
+    for s in range(b):
+        for slot in range(K if residual else K + 1):
+            F = orc.draw_cdf(target, draft, T, s, slot, residual)
+            p = special.softmax(W.as_f32(target[s, slot]).astype(np.float64) / T)
+            w = p
+            if residual:
+                q = special.softmax(W.as_f32(draft[s, slot]).astype(np.float64) / T)
+                w = np.maximum(0.0, p - q)
+            ref = np.cumsum(w)
+            assert np.abs(F - ref).max() <= 1e-13, (s, slot, np.abs(F - ref).max())
+            assert np.all(np.diff(F) >= 0.0)
+
+
+def test_draw_cdf_rejects_bad_arguments(orc):
+    rng = np.random.default_rng(30)
+    target = _rows(rng, 3, 50, "f32", 1.0).reshape(1, 3, 50)
+    draft = _rows(rng, 2, 50, "f32", 1.0).reshape(1, 2, 50)
+    with pytest.raises(ValueError):
+        orc.draw_cdf(target, draft, 0.0, 0, 0, False)        # T must be > 0
+    with pytest.raises(ValueError):
+        orc.draw_cdf(target, draft, 1.0, 0, 2, True)         # no residual at the bonus slot

@@ -134,6 +134,7 @@ MARKOV_CASES = [
     ("vocab4", 3, 2, 4, 64, 8, 0.5),
     ("one_tile_and_a_bit", 5, 3, 132, 128, 8, 0.5),
     ("single_sequence", 1, 7, 4096, 256, 16, 0.5),
+    ("vocab_over_1M_segments_in_memory", 2, 2, 1100000, 64, 8, 0.5),
 ]
 
 

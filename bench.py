@@ -557,6 +557,31 @@ def main_markov(args) -> int:
     return 0
 
 
+def read_ceiling(stream, nbytes: int = 1 << 30, launches: int = 20) -> dict:
+    """The achievable read bandwidth beside the spec peak: spec_stream_read
+    (the row pass's load shape) over 1 GiB, larger than every cache, median of
+    `launches` event-timed launches on the bench's stream."""
+    import numpy as np
+    import torch
+    import lossless_draft_verification_amd as L
+    src = torch.empty(nbytes, dtype=torch.uint8, device=stream.device)
+    sink = torch.zeros(1, dtype=torch.int32, device=stream.device)
+    for _ in range(3):
+        L.stream_read(src, sink, stream=stream)
+    ts = []
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.stream_read(src, sink, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del src
+    return {"kernel": "stream_read_kernel (read-only, 1 GiB, the row pass's load shape)",
+            "GBs": nbytes / (ms * 1e-3) / 1e9, "peak_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -769,6 +794,7 @@ def main() -> int:
     else:
         dom, dom_bytes, dom_ms = "row_pass", bytes_greedy, stage["greedy_row_pass"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    ceiling = read_ceiling(stream)
     wl_key = (f"c{args.workload}_{args.step}" + ("_ragged" if args.ragged else "")
               + (f"_sharded{args.sharded}" if args.sharded else ""))
     traffic = load_traffic(dom, wl_key)
@@ -810,6 +836,7 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": dom_ms,
+            "ceiling": dict(ceiling, frac=achieved / ceiling["GBs"]),
         },
         "step_hbm": {
             "algorithmic_bytes_per_step": bytes_step,

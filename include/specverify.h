@@ -337,6 +337,17 @@ int spec_set_stage_events(void *const *events, int n_events);
  */
 int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream);
 
+/*
+ * Read-only stream over nbytes at src (a multiple of 16, 16-byte aligned)
+ * with the row pass's shape: one single-wave workgroup per 16 KiB, 16
+ * nontemporal 16-byte loads per lane issued together.  It measures the
+ * achievable read bandwidth that the row pass is compared with.  sink (a
+ * device word, 4-byte aligned) is written only if the folded data equal one
+ * fixed value, so the loads are kept; its contents are otherwise untouched.
+ * Returns SPEC_EINVAL / SPEC_ELAUNCH on error.
+ */
+int spec_stream_read(const void *src, size_t nbytes, uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_
            "sharded_mixed_accept", "sharded_workspace_bytes",
            "DraftBlock", "markov_block_decode", "markov_workspace_bytes",
            "workspace_bytes", "mixed_workspace_bytes",
-           "set_stage_events", "stream_copy", "library_path", "SpecError"]
+           "set_stage_events", "stream_copy", "stream_read", "library_path", "SpecError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
@@ -90,6 +90,8 @@ def _load():
     lib.spec_set_stage_events.restype = i32
     lib.spec_stream_copy.argtypes = [vp, vp, sz, vp]
     lib.spec_stream_copy.restype = i32
+    lib.spec_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.spec_stream_read.restype = i32
     return lib
 
 
@@ -521,6 +523,16 @@ def set_stage_events(events: Optional[Sequence[torch.cuda.Event]]) -> None:
     arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
     _stage_keepalive = (arr, list(events))
     _check(_lib.spec_set_stage_events(ctypes.cast(arr, ctypes.c_void_p), len(events)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read-only stream over src with the row pass's load shape (bandwidth
+    ceiling); sink is a device int32 tensor the kernel may write."""
+    _on_gpu(src, sink)
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("sink must be a device int32 tensor")
+    n = src.numel() * src.element_size()
+    _check(_lib.spec_stream_read(src.data_ptr(), n, sink.data_ptr(), _stream_handle(src.device, stream)))
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -207,3 +207,12 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(2, 7, dtype=torch.int32)
     with pytest.raises(ValueError):
         L.greedy_accept(t, x)
+
+
+def test_stream_read_validation(lib):
+    assert lib.spec_stream_read(None, 16, 16, None) == 1      # null source
+    assert lib.spec_stream_read(16, 16, None, None) == 1      # null sink
+    assert lib.spec_stream_read(16, 15, 16, None) == 1        # not a multiple of 16 bytes
+    assert lib.spec_stream_read(24, 16, 16, None) == 1        # misaligned source
+    assert lib.spec_stream_read(16, 16, 18, None) == 1        # misaligned sink
+    assert lib.spec_stream_read(16, 0, 16, None) == 0         # nothing to read

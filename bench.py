@@ -534,6 +534,22 @@ def main_markov(args) -> int:
     per_pos = V * r * 2 + b * V * 4 * 2 + b * r * 2 + bs * SEG_BYTES
     loop_bytes = K * per_pos
     achieved = loop_bytes / (loop_ms * 1e-3) / 1e9
+    # The correction kernel's traffic is two streams read for one written.  A
+    # plain stream of that mix at the same size (two 134 MB float32 rows added
+    # into a third, torch's elementwise kernel) is the reference for it.
+    mix = [torch.empty(b * V, dtype=torch.float32, device=dev) for _ in range(3)]
+    for _ in range(3):
+        torch.add(mix[0], mix[1], out=mix[2])
+    mix_ts = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.add(mix[0], mix[1], out=mix[2])
+        e1.record(stream)
+        e1.synchronize()
+        mix_ts.append(e0.elapsed_time(e1))
+    mix_gbs = 3 * b * V * 4 / (float(np.median(mix_ts)) * 1e-3) / 1e9
+    del mix
     result = {
         "metric": "draft blocks/s (Markov-head block decode), b=128 K=7 V=262144 r=256",
         "value": b / (ms * 1e-3), "unit": "draft blocks/s", "n_gpus": 1, "steps": args.steps,
@@ -544,7 +560,10 @@ def main_markov(args) -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "position loop (markov_stream_kernel + draft_select_kernel, 7 positions)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms},
+                     "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms,
+                     "ceiling": {"kernel": "torch.add over two 134 MB float32 rows into a third (2 reads : 1 write, "
+                                           "the correction kernel's mix)",
+                                 "GBs": mix_gbs, "peak_frac": mix_gbs / HBM_PEAK_GBS, "frac": achieved / mix_gbs}},
         "stage_ms": {"position_loop": loop_ms, "confidence": conf_ms},
         "staged_ms_per_step": staged / args.steps,
         "mean_draft_length": float(out.lengths.float().mean().item()),

@@ -135,6 +135,7 @@ MARKOV_CASES = [
     ("one_tile_and_a_bit", 5, 3, 132, 128, 8, 0.5),
     ("single_sequence", 1, 7, 4096, 256, 16, 0.5),
     ("vocab_over_1M_segments_in_memory", 2, 2, 1100000, 64, 8, 0.5),
+    ("three_seq_tiles_many_vocab_tiles", 300, 2, 100000, 64, 8, 0.5),
 ]
 
 

@@ -297,8 +297,8 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
  *   workspace       spec_markov_workspace_bytes(b, K, V, r) bytes, 256-byte aligned
  * Two kernels per position (the correction on the matrix cores with the base
  * logits added, q_i stored and per-tile records; then per sequence the merge
- * of the tile records, the pick and the draw), then the confidence and length
- * kernels.  For r <= 256 with 16-byte aligned base rows the correction kernel
+ * of the tile records, the pick and the draw), then one kernel for the
+ * confidences and the lengths.  For r <= 256 with 16-byte aligned base rows the correction kernel
  * is a persistent one-workgroup-per-CU stream; other shapes take a tiled
  * kernel with the same results.
  */

@@ -1645,15 +1645,11 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     if (want_conf) {
         const int vec = (uintptr_t)hidden % 16 == 0 && h_row_stride % 8 == 0 && h_batch_stride % 8 == 0 &&
                         (uintptr_t)conf_w % 16 == 0;
-        hipLaunchKernelGGL(confidence_kernel, dim3((unsigned)(b * K)), dim3(kWave), 0, st, (const uint16_t *)hidden,
-                           h_batch_stride, h_row_stride, D, (const uint16_t *)w1, w1_row_stride, r,
-                           (const uint16_t *)conf_w, conf_b, anchors, (const int32_t *)tokens, K, V, vec, confidence);
+        hipLaunchKernelGGL(confidence_length_kernel, dim3((unsigned)b), dim3(kConfWaves * kWave), 0, st,
+                           (const uint16_t *)hidden, h_batch_stride, h_row_stride, D, (const uint16_t *)w1,
+                           w1_row_stride, r, (const uint16_t *)conf_w, conf_b, anchors, (const int32_t *)tokens, K, V,
+                           vec, confidence, threshold, lengths);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        if (lengths) {
-            hipLaunchKernelGGL(draft_length_kernel, dim3((unsigned)((b + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
-                               (const float *)confidence, b, K, threshold, lengths);
-            if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
-        }
     }
     stage_mark(2, st);
     return SPEC_OK;

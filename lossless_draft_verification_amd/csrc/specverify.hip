@@ -783,9 +783,13 @@ __device__ inline void search_segment(const void *tp, const void *dp, int64_t e_
 // Draw the token of slot n of sequence s (one 256-thread block): inverse CDF
 // over ascending vocabulary index of the residual (mode residual, residual
 // segments) or of p_n (mode target, row-pass segments: the bonus, or a
-// rejected slot whose residual mass is zero).
+// rejected slot whose residual mass is zero).  `pl` is the sequence's plan,
+// `tpart` the segment records of its slot n (global memory or LDS), `rm` its
+// residual masses with this thread's first one preloaded in `rm_first` (both
+// unused without a residual draw).
 template <int DT, bool VEC>
-__device__ inline void draw_seq(const Ctx &c, int s) {
+__device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const Partial *tpart, const double *rm,
+                                 double rm_first) {
     const int t = threadIdx.x;
     const int K = c.K, V = c.V, nseg = c.nseg, nres = c.nres;
     __shared__ double sw[kWavesPerBlock];
@@ -794,21 +798,14 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
     __shared__ int32_t sY;
     __shared__ int32_t sLastPos;
 
-    // The residual masses of this thread's range are loaded together with the
-    // plan (their address does not depend on it); unused when the plan says
-    // otherwise.
-    const double *rm = c.rmass + (int64_t)s * nres;
     const int rper = (nres + kBlock - 1) / kBlock;
     const int r0 = min(nres, t * rper);
-    const double rm_first = r0 < min(nres, r0 + rper) ? rm[r0] : 0.0;
-    const DrawPlan pl = c.plan[s];
     if (pl.mode == kModeNone) return;
     const bool sharded = c.shard_id >= 0;
     if (sharded && pl.shard != c.shard_id) return;
     float c_hi, c_lo;
     double c64;
     split_scale(pl.T, c_hi, c_lo, c64);
-    const Partial *tpart = c.part + ((int64_t)s * c.rps + pl.slot) * nseg;
     bool resid = pl.mode == kModeResidual;
 
     // (a) segment masses: thread t sums a contiguous range of segments.
@@ -886,6 +883,21 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
         if (y < 0) y = (int32_t)min((int64_t)V - 1, (int64_t)seg * (resid ? rseg_elems(DT) : seg_elems(DT)));
         c.tok[(int64_t)s * (K + 1) + pl.slot] = y + c.col0;
     }
+}
+
+// The draw of sequence s from the plan and records in the workspace.
+template <int DT, bool VEC>
+__device__ inline void draw_seq(const Ctx &c, int s) {
+    // The residual masses of this thread's range are loaded together with the
+    // plan (their address does not depend on it); unused when the plan says
+    // otherwise.
+    const int nres = c.nres;
+    const double *rm = c.rmass + (int64_t)s * nres;
+    const int rper = (nres + kBlock - 1) / kBlock;
+    const int r0 = min(nres, (int)threadIdx.x * rper);
+    const double rm_first = r0 < min(nres, r0 + rper) ? rm[r0] : 0.0;
+    const DrawPlan pl = c.plan[s];
+    draw_core<DT, VEC>(c, s, pl, c.part + ((int64_t)s * c.rps + pl.slot) * c.nseg, rm, rm_first);
 }
 
 // ---------------------------------------------------------------------------
@@ -1576,7 +1588,6 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     // 128-sequence span fits a 31-bit offset: the persistent streaming kernel,
     // one workgroup per CU.
     static_assert(kMsMaxR == 256, "one streaming instance per r / 64 in 1..4");
-    uint16_t *ubuf = (uint16_t *)(ws + L.ubuf_off);        // [b, r]: W1 rows of the last drawn tokens
     const bool streaming = r <= kMsMaxR && (uintptr_t)base % 16 == 0 && base_batch_stride % 4 == 0 &&
                            base_row_stride % 4 == 0 && (int64_t)(kMsBH - 1) * base_batch_stride * 4 + 128 < INT_MAX;
     MsArgs sa = {};
@@ -1620,7 +1631,6 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         if (streaming) {
             sa.prev = prev;
             sa.pstride = pstride;
-            sa.ubuf = i == 0 ? nullptr : ubuf;          // from position 1 on, the rows the select copied
             sa.step = i;
             switch (r / 64) {
             case 1: hipLaunchKernelGGL(markov_stream_kernel<2>, dim3(grid_s), dim3(kMsThreads), 0, st, sa); break;
@@ -1637,8 +1647,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
         }
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
         hipLaunchKernelGGL(draft_select_kernel, dim3((unsigned)b), dim3(kBlock), 0, st, c, i,
-                           (const Partial *)ma.tpart, L.ntiles, prev, pstride, (const uint16_t *)w1, w1_row_stride, r,
-                           streaming && i + 1 < K ? ubuf : nullptr);
+                           (const Partial *)ma.tpart, L.ntiles, prev, pstride);
         if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     }
     stage_mark(1, st);

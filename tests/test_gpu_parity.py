@@ -194,6 +194,34 @@ def test_mixed_small(dtype):
     _check(compare_mixed(case, temps, *out, f"mixed_small_{dtype}"), f"mixed_small_{dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_temperatures_and_masked_vocab(dtype):
+    """Very peaked and very flat softmaxes (T from 0.02 to 50) next to greedy
+    rows, and valid rows whose vocabulary is partly masked with -inf: target
+    columns 1000..8999 and draft columns 5000..12999 of sequences 5..9, so a
+    draft token can have q(x) = 0 < p(x) (accepted), p(x) = 0 (rejected) or
+    both zero (rejected), and the residual and bonus draws must skip the
+    masked columns."""
+    import dataclasses
+    b, K, V = 10, 5, 30011
+    case = W.make_case("extreme", b=b, K=K, V=V, dtype=dtype, target_scale=2.5,
+                       draft_sigma=(0.2, 1.5), T=1.0, seed=61)
+    t, d, x = case.target.copy(), case.draft.copy(), case.draft_tokens.copy()
+    ninf = np.uint16(0xFF80) if t.dtype == np.uint16 else np.float32(-np.inf)
+    t[5:, :, 1000:9000] = ninf
+    d[5:, :, 5000:13000] = ninf
+    x[5:, 0] = [1500, 6000, 10000, 20000, 7000]      # p = 0; both 0; q = 0; neither; both 0
+    case = dataclasses.replace(case, target=t, draft=d, draft_tokens=x)
+    temps = np.array([0.0, 0.02, 0.05, 20.0, 50.0, 0.0, 0.02, 0.7, 20.0, 1.0])
+    out = run_gpu_mixed(case, temps)
+    assert (out[0] >= 0).all()
+    # every committed token of a masked sequence has p > 0: none in the target mask
+    committed = out[1][5:]
+    committed = committed[committed >= 0]
+    assert not ((committed >= 1000) & (committed < 9000)).any()
+    _check(compare_mixed(case, temps, *out, f"extreme_masked_{dtype}"), f"extreme_masked_{dtype}")
+
+
 def test_mixed_matches_single_rule_calls():
     """A mixed batch whose sequences all share one rule equals the single-rule
     entry point bit for bit (same Philox rows)."""

@@ -68,12 +68,16 @@ def _compare(case: W.MarkovCase, gpu, res, threshold, name) -> Report:
         diverged = False
         for i in range(case.K):
             prev = case.anchors[s] if i == 0 else tok_o[s, i - 1]
-            tol = g_r * (np.abs(w1f[prev]) @ w2a.T) + 2.0 ** -23 * np.abs(q_o[s, i])
-            err = np.abs(q_g[s, i].astype(np.float64) - q_o[s, i])
-            max_ratio = max(max_ratio, float((err / tol).max()))
-            if not (err <= tol).all():
+            # non-finite oracle entries (a base logit masked with -inf) must be
+            # matched exactly; the bound applies to the finite ones
+            fin = np.isfinite(q_o[s, i])
+            tol = np.where(fin, g_r * (np.abs(w1f[prev]) @ w2a.T) + 2.0 ** -23 * np.abs(np.where(fin, q_o[s, i], 0.0)),
+                           0.0)
+            err = np.where(fin, np.abs(q_g[s, i].astype(np.float64) - np.where(fin, q_o[s, i], 0.0)), 0.0)
+            max_ratio = max(max_ratio, float((err / np.where(fin, tol, 1.0)).max()))
+            if not ((err <= tol).all() and (q_g[s, i][~fin] == q_o[s, i][~fin]).all()):
                 rep.failures.append(dict(case=name, seq=s, pos=i, what="corrected logits",
-                                         worst=float((err / tol).max())))
+                                         worst=float((err / np.where(fin, tol, 1.0)).max())))
                 diverged = True
                 break
             if abs(conf_g[s, i] - res["confidence"][s, i]) > 1e-6:
@@ -148,6 +152,25 @@ def test_markov_block_decode(spec):
     res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
                           conf_w=case.conf_w, conf_b=case.conf_b, threshold=thr)
     _check(_compare(case, gpu, res, thr, f"markov_{name}"), f"markov_{name}")
+
+
+def test_markov_extreme_temperatures_and_masked_vocab():
+    """Temperatures from 0.02 to 50 next to greedy rows on the streaming
+    correction kernel (r = 256), and sequences 5..9 with base logits masked
+    to -inf on columns 1000..8999 (q = -inf there): no draw or argmax may
+    land in the mask."""
+    import dataclasses
+    case = W.make_markov_case("mext", b=10, K=5, V=20012, r=256, D=32, rule=W.SAMPLING, T=1.0, seed=71)
+    temps = np.array([0.0, 0.02, 0.05, 20.0, 50.0, 0.0, 0.02, 0.7, 20.0, 1.0])
+    base = case.base.copy()
+    base[5:, :, 1000:9000] = -np.inf
+    case = dataclasses.replace(case, base=base, temps=temps)
+    gpu = _run(case, 0.5)
+    tok = gpu[0][5:]
+    assert (tok >= 0).all() and not ((tok >= 1000) & (tok < 9000)).any()
+    res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
+                          conf_w=case.conf_w, conf_b=case.conf_b, threshold=0.5)
+    _check(_compare(case, gpu, res, 0.5, "markov_extreme_masked"), "markov_extreme_masked")
 
 
 def test_markov_invalid_inputs():

@@ -79,6 +79,14 @@ def load_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def markov_loop_traffic(K: int):
+    """HBM bytes of the Markov position loop (K correction and select
+    launches) from the counters of one launch of each, or None."""
+    a = load_traffic("markov_stream", "markov_b128_V262144_r256")
+    c = load_traffic("draft_select", "markov_b128_V262144_r256")
+    return None if a is None or c is None else K * (a + c)
+
+
 def cpu_baseline(case, greedy_idx, sample_idx, budget_s: float):
     """Time the CPU oracle (single thread) on whole sequences of the workload,
     alternating greedy and sampling sequences until the budget is spent."""
@@ -111,7 +119,18 @@ def cpu_baseline(case, greedy_idx, sample_idx, budget_s: float):
 
 
 KERNEL_KEYS = {"row_pass": "row_pass", "scan_kernel": "scan", "residual_kernel": "residual_mass",
-               "draw_kernel": "draw_token", "stream_copy_kernel": "stream_copy"}
+               "draw_kernel": "draw_token", "stream_copy_kernel": "stream_copy",
+               "lm_head_dl_kernel": "lm_head_gemm", "markov_stream_kernel": "markov_stream",
+               "draft_select_kernel": "draft_select"}
+
+# Counter passes over the other bench modes: (-o prefix, kernels, workload key,
+# profile file the counters are appended to, bench arguments).
+EXTRA_PMC = [
+    ("fused", ("lm_head_gemm",), "fused_b128_V262144_D3840", "lm_head_fused_verify_b128_V262144_D3840.md",
+     "--fused --steps 2 --warmup 1 --no-cpu-baseline --no-reference"),
+    ("markov", ("markov_stream", "draft_select"), "markov_b128_V262144_r256",
+     "markov_block_decode_b128_V262144_r256.md", "--markov --steps 2 --warmup 1 --no-cpu-baseline"),
+]
 
 
 def _short(name: str) -> str:
@@ -191,6 +210,30 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
     lines += ["", "Algorithmic bytes of the row pass per launch: 771751936 (every logit read once).", ""]
     with open(os.path.join(prof, "verify_c5_mixed.md"), "w") as f:
         f.write("\n".join(lines))
+    # the fused and Markov paths' kernels, appended to their trace summaries
+    for mode, keys, wl, fname, bargs in EXTRA_PMC:
+        fp, wp = (os.path.join(pmc, f"{mode}_{c}_counter_collection.csv") for c in ("FETCH_SIZE", "WRITE_SIZE"))
+        if not (os.path.exists(fp) and os.path.exists(wp)):
+            continue
+        fm, wm = counter(fp), counter(wp)
+        sec = ["", "## Counters (rocprofv3 --pmc, one counter per run), KiB per dispatch", "",
+               "Commands (scaled as in verify_c5_mixed.md: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f):" % (f_scale, w_scale),
+               "",
+               f"    rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc -o {mode}_FETCH_SIZE --output-format csv \\",
+               f"        -- python3 $R/bench.py {bargs}",
+               f"    rocprofv3 --pmc WRITE_SIZE  (same, -o {mode}_WRITE_SIZE)", "",
+               "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) | HBM bytes per dispatch (scaled) |",
+               "|---|---|---|---|---|"]
+        for k in keys:
+            if k not in fm:
+                continue
+            f_med, w_med = statistics.median(fm[k]), statistics.median(wm.get(k, [0.0]))
+            byts = (f_med * f_scale + w_med * w_scale) * 1024.0
+            traffic[k] = {wl: {"bytes_per_launch": byts, "fetch_kib": f_med, "write_kib": w_med,
+                               "fetch_scale": f_scale, "write_scale": w_scale, "source_sha256_16": digest}}
+            sec.append(f"| {k} | {len(fm[k])} | {f_med:.0f} | {w_med:.0f} | {byts:.0f} |")
+        with open(os.path.join(prof, fname), "a") as f:
+            f.write("\n".join(sec) + "\n")
     with open(os.path.join(prof, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     print("\n".join(lines))
@@ -430,7 +473,8 @@ def main_fused(args) -> int:
                    "step": "one spec_fused_mixed_accept call", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "lm_head_dl_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_flops_per_launch": gemm_flops,
+                     "traffic": load_traffic("lm_head_gemm", "fused_b128_V262144_D3840"),
+                     "algorithmic_flops_per_launch": gemm_flops,
                      "avg_launch_ms": stage["lm_head_gemm"]},
         "step_hbm": {"algorithmic_bytes_per_step": step_bytes,
                      "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -560,7 +604,8 @@ def main_markov(args) -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "position loop (markov_stream_kernel + draft_select_kernel, 7 positions)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": loop_bytes, "avg_launch_ms": loop_ms,
+                     "traffic": markov_loop_traffic(K), "algorithmic_bytes_per_launch": loop_bytes,
+                     "avg_launch_ms": loop_ms,
                      "ceiling": {"kernel": "torch.add over two 134 MB float32 rows into a third (2 reads : 1 write, "
                                            "the correction kernel's mix)",
                                  "GBs": mix_gbs, "peak_frac": mix_gbs / HBM_PEAK_GBS, "frac": achieved / mix_gbs}},

@@ -677,7 +677,7 @@ def main() -> int:
         print("--ragged and --sharded need --step mixed", file=sys.stderr)
         return 2
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the verify step shards by sequence with no exchange; see the design notes).",
               file=sys.stderr)
         return 2

@@ -302,3 +302,40 @@ def test_workload_c5_ragged():
     temps = np.where(case.rule == W.GREEDY, 0.0, case.T)
     out = run_gpu_mixed(case, temps, lens=lens)
     _check(compare_mixed(case, temps, *out, "c5_ragged", lens=lens), "workload_c5_ragged")
+
+
+# ------------------------------------------------------------- seeded sweep
+
+
+def _sweep_case(k: int):
+    """Seeded random shape, dtype, value distribution, per-sequence rule and
+    temperature (some invalid), and draft lengths (half the cases)."""
+    rng = np.random.default_rng(5000 + k)
+    b = int(rng.integers(1, 33))
+    K = int(rng.integers(1, 13))
+    V = int(rng.choice([1, 2, 5, 7, 8, 9, 100, 1000, 4097, 8191, 8193, 16384, 20011, 65537]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    kind = str(rng.choice(["normal", "zipf"]))
+    rules = np.where(rng.random(b) < 0.5, W.GREEDY, W.SAMPLING).astype(np.int32)
+    case = W.make_case(f"sweep{k}", b=b, K=K, V=V, dtype=dtype, target_kind=kind,
+                       target_scale=float(rng.uniform(0.5, 4.0)), draft_sigma=(0.05, 2.0), rule=rules,
+                       T=0.9, seed=int(rng.integers(1 << 30)))
+    temps = np.where(rules == W.GREEDY, 0.0, rng.choice([0.3, 0.8, 1.0, 2.5], size=b))
+    bad = rng.random(b) < 0.1
+    temps[bad] = rng.choice([-1.0, np.nan, np.inf], size=int(bad.sum()))
+    lens = rng.integers(0, K + 1, size=b).astype(np.int32) if k % 2 else None
+    if lens is not None:
+        case = _ragged_case(case, lens)
+    return case, temps, lens
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_seeded_sweep(k):
+    """Sixteen seeded random mixed calls (shapes from V = 1 to a few tiles past
+    65536, both dtypes, normal and Zipf rows, invalid temperatures, ragged
+    lengths) against the oracle."""
+    case, temps, lens = _sweep_case(k)
+    out = run_gpu_mixed(case, temps, lens=lens)
+    name = f"sweep_{k}"
+    _check(compare_mixed(case, temps, *out, name, lens=lens), name)
+

@@ -204,3 +204,33 @@ def test_markov_deterministic_repeat():
     a, c = _run(case, 0.5), _run(case, 0.5)
     for x, y in zip(a, c):
         np.testing.assert_array_equal(x, y)
+
+
+def _markov_sweep_case(k: int):
+    """Seeded random b, K, V, rank (both correction kernels), per-sequence
+    rule and temperature, and confidence threshold.  (Invalid inputs are
+    covered by test_markov_invalid_inputs: the oracle numbers the Philox rows
+    by position in the batch it is given, so the sweep keeps every row.)"""
+    rng = np.random.default_rng(7000 + k)
+    b = int(rng.integers(1, 150))
+    K = int(rng.integers(1, 8))
+    if k % 2 == 0:                       # the streaming kernel: rank <= 256, 16-byte aligned base rows
+        V = int(rng.choice([4, 64, 1000, 4096, 9000, 20012]))
+        r = int(rng.choice([64, 128, 192, 256]))
+    else:
+        V = int(rng.choice([3, 64, 129, 1000, 4097, 9000, 20011]))
+        r = int(rng.choice([64, 128, 192, 256, 320, 384]))
+    rules = np.where(rng.random(b) < 0.5, W.GREEDY, W.SAMPLING).astype(np.int32)
+    case = W.make_markov_case(f"msweep{k}", b=b, K=K, V=V, r=r, D=int(rng.choice([8, 32, 64])), rule=rules,
+                              T=float(rng.choice([0.3, 0.8, 2.0])), seed=int(rng.integers(1 << 30)))
+    return case, float(rng.choice([0.0, 0.5, 0.7]))
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_markov_seeded_sweep(k):
+    """Eight seeded random Markov block decodes against the oracle."""
+    case, thr = _markov_sweep_case(k)
+    gpu = _run(case, thr)
+    res = OM.block_decode(case.base, case.anchors, case.w1, case.w2, case.temps, case.seeds, hidden=case.hidden,
+                          conf_w=case.conf_w, conf_b=case.conf_b, threshold=thr)
+    _check(_compare(case, gpu, res, thr, f"markov_sweep_{k}"), f"markov_sweep_{k}")

@@ -149,3 +149,32 @@ def test_fused_deterministic_repeat():
     a, c = _run_fused(case), _run_fused(case)
     for x, y in zip(a, c):
         np.testing.assert_array_equal(x, y)
+
+
+def _fused_sweep_case(k: int):
+    """Seeded random b, K, V, D (a multiple of 64), softcap, per-sequence
+    rule and temperature (some invalid) and, in odd cases, draft lengths."""
+    rng = np.random.default_rng(9000 + k)
+    b = int(rng.integers(1, 71))
+    K = int(rng.integers(1, 8))
+    V = int(rng.choice([7, 300, 4097, 9000, 20011]))
+    D = int(rng.choice([64, 128, 192, 256, 512]))
+    cap = float(rng.choice([0.0, 30.0]))
+    rule = np.where(rng.random(b) < 0.5, W.GREEDY, W.SAMPLING).astype(np.int32)
+    case = W.make_fused_case(f"fsweep{k}", b=b, K=K, V=V, D=D, softcap=cap, rule=rule,
+                             T=float(rng.choice([0.5, 0.8, 1.5])), seed=int(rng.integers(1 << 30)))
+    bad = rng.random(b) < 0.08
+    case.temps[bad] = rng.choice([-1.0, np.inf], size=int(bad.sum()))
+    lens = rng.integers(0, K + 1, size=b).astype(np.int32) if k % 2 else None
+    return case, lens
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_fused_seeded_sweep(k):
+    """Six seeded random fused calls (one row tile to several, V from 7 to a
+    ragged 20011, D from 64 to 512, softcap on and off) against the oracle."""
+    case, lens = _fused_sweep_case(k)
+    out = _run_fused(case, lens)
+    res, tol = _oracle(case, lens=lens)
+    _check(compare_fused(case, res, tol, *out, f"fused_sweep_{k}", lens=lens), f"fused_sweep_{k}")
+

@@ -120,3 +120,27 @@ def test_sharded_deterministic_repeat():
     a, c = _run(case, temps, [4000, 5000, 3000]), _run(case, temps, [4000, 5000, 3000])
     for x, y in zip(a, c):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_sharded_seeded_sweep(k):
+    """Six seeded random splits (1 to 12 shards of uneven widths, some of one
+    column), both dtypes, per-sequence rules and temperatures, draft lengths
+    in odd cases: equal to the oracle and to the unsharded call."""
+    rng = np.random.default_rng(11000 + k)
+    b, K = int(rng.integers(1, 40)), int(rng.integers(1, 9))
+    V = int(rng.choice([50, 3000, 20011, 40000]))
+    G = int(rng.integers(1, min(12, V) + 1))
+    cuts = np.sort(rng.choice(np.arange(1, V), size=G - 1, replace=False)) if G > 1 else np.array([], int)
+    widths = [int(x) for x in np.diff(np.concatenate([[0], cuts, [V]]))]
+    dt = str(rng.choice(["bf16", "f32"]))
+    case = W.make_case(f"shsweep{k}", b=b, K=K, V=V, dtype=dt, target_scale=2.5, draft_sigma=(0.1, 1.5), T=0.8,
+                       seed=int(rng.integers(1 << 30)))
+    temps = np.where(rng.random(b) < 0.4, 0.0, rng.choice([0.5, 0.8, 1.3], size=b))
+    lens = rng.integers(0, K + 1, size=b).astype(np.int32) if k % 2 else None
+    out = _run(case, temps, widths, lens)
+    _check(compare_mixed(case, temps, *out, f"sharded_sweep_{k}", lens=lens), f"sharded_sweep_{k}")
+    ref = _run_unsharded(case, temps, lens)
+    for a, r in zip((out[0], out[1], out[4]), (ref[0], ref[1], ref[4])):
+        np.testing.assert_array_equal(a, r)
+

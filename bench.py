@@ -130,6 +130,10 @@ EXTRA_PMC = [
      "--fused --steps 2 --warmup 1 --no-cpu-baseline --no-reference"),
     ("markov", ("markov_stream", "draft_select"), "markov_b128_V262144_r256",
      "markov_block_decode_b128_V262144_r256.md", "--markov --steps 2 --warmup 1 --no-cpu-baseline"),
+    ("ragged", ("row_pass",), "c5_mixed_ragged", "verify_c5_mixed.md",
+     "--ragged --steps 3 --warmup 1 --no-cpu-baseline --no-reference"),
+    ("sharded", ("row_pass",), "c5_mixed_sharded8", "verify_c5_vocab_sharded8.md",
+     "--sharded 8 --steps 3 --warmup 1 --no-cpu-baseline --no-reference"),
 ]
 
 
@@ -216,7 +220,8 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
         if not (os.path.exists(fp) and os.path.exists(wp)):
             continue
         fm, wm = counter(fp), counter(wp)
-        sec = ["", "## Counters (rocprofv3 --pmc, one counter per run), KiB per dispatch", "",
+        sec = ["", f"## Counters of the `{bargs.split()[0]}` bench (rocprofv3 --pmc, one counter per run), "
+                   "KiB per dispatch", "",
                "Commands (scaled as in verify_c5_mixed.md: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f):" % (f_scale, w_scale),
                "",
                f"    rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc -o {mode}_FETCH_SIZE --output-format csv \\",
@@ -229,8 +234,9 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
                 continue
             f_med, w_med = statistics.median(fm[k]), statistics.median(wm.get(k, [0.0]))
             byts = (f_med * f_scale + w_med * w_scale) * 1024.0
-            traffic[k] = {wl: {"bytes_per_launch": byts, "fetch_kib": f_med, "write_kib": w_med,
-                               "fetch_scale": f_scale, "write_scale": w_scale, "source_sha256_16": digest}}
+            traffic.setdefault(k, {})[wl] = {"bytes_per_launch": byts, "fetch_kib": f_med, "write_kib": w_med,
+                                             "fetch_scale": f_scale, "write_scale": w_scale,
+                                             "source_sha256_16": digest}
             sec.append(f"| {k} | {len(fm[k])} | {f_med:.0f} | {w_med:.0f} | {byts:.0f} |")
         with open(os.path.join(prof, fname), "a") as f:
             f.write("\n".join(sec) + "\n")

@@ -216,3 +216,16 @@ def test_stream_read_validation(lib):
     assert lib.spec_stream_read(24, 16, 16, None) == 1        # misaligned source
     assert lib.spec_stream_read(16, 16, 18, None) == 1        # misaligned sink
     assert lib.spec_stream_read(16, 0, 16, None) == 0         # nothing to read
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a
+    message, before touching any device."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

@@ -155,9 +155,11 @@ def _fused_sweep_case(k: int):
     """Seeded random b, K, V, D (a multiple of 64), softcap, per-sequence
     rule and temperature (some invalid) and, in odd cases, draft lengths."""
     rng = np.random.default_rng(9000 + k)
-    b = int(rng.integers(1, 71))
     K = int(rng.integers(1, 8))
     V = int(rng.choice([7, 300, 4097, 9000, 20011]))
+    b = int(rng.integers(1, min(70, V // (K + 1)) + 1)) if V >= K + 1 else 1   # distinct planted tokens
+    if V < b * (K + 1):
+        V = b * (K + 1)
     D = int(rng.choice([64, 128, 192, 256, 512]))
     cap = float(rng.choice([0.0, 30.0]))
     rule = np.where(rng.random(b) < 0.5, W.GREEDY, W.SAMPLING).astype(np.int32)

@@ -42,6 +42,23 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def settle(step, seconds: float, chunk: int = 50):
+    """Run `step` in chunks of untimed calls until `seconds` of wall time have
+    passed (the GPU's clocks ramp up under sustained load, whatever the
+    warm-up count).  Returns (wall seconds, steps run)."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        for _ in range(chunk):
+            step(k)
+            k += 1
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return el, k
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -400,6 +417,8 @@ def main_fused(args) -> int:
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    settle_s, settle_steps = settle(step, args.settle, chunk=10)
+    log(f"settled clocks: {settle_steps} untimed steps in {settle_s:.2f}s")
     log(f"region 1: {args.steps} timed fused steps")
     total_ms = timed(step, args.steps)
     ms_per_step = total_ms / args.steps
@@ -468,6 +487,8 @@ def main_fused(args) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": settle_s,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -568,6 +589,8 @@ def main_markov(args) -> int:
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    settle_s, settle_steps = settle(step, args.settle, chunk=10)
+    log(f"settled clocks: {settle_steps} untimed steps in {settle_s:.2f}s")
     total_ms = timed(step, args.steps)
     ms = total_ms / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -603,7 +626,8 @@ def main_markov(args) -> int:
     result = {
         "metric": "draft blocks/s (Markov-head block decode), b=128 K=7 V=262144 r=256",
         "value": b / (ms * 1e-3), "unit": "draft blocks/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_s": settle_s, "settle_steps": settle_steps,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "markov: " + W.MARKOV_TEXT, "b": b, "K": K, "V": V, "r": r, "D": D,
                    "confidence_threshold": 0.6, "step": "one spec_markov_block_decode call",
@@ -656,8 +680,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps first; about 1000 (0.15 s) lets the GPU clocks settle")
+    ap.add_argument("--warmup", type=int, default=1000, help="untimed steps first")
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="after the warm-up, untimed steps for at least this much wall time, "
+                         "whatever --warmup is, so the GPU clocks have ramped up before timing")
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--step", choices=["mixed", "split"], default="mixed")
     ap.add_argument("--copies", type=int, default=4)
@@ -806,6 +832,8 @@ def main() -> int:
     for k in range(args.warmup):
         main_step(k)
     torch.cuda.synchronize()
+    settle_s, settle_steps = settle(main_step, args.settle)
+    log(f"settled clocks: {settle_steps} untimed steps in {settle_s:.2f}s")
 
     log(f"region 1: {args.steps} timed steps")
     total_ms = timed(main_step, args.steps)
@@ -876,6 +904,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": settle_s,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -42,7 +42,7 @@ extern "C" {
 
 typedef enum {
     SPEC_OK = 0,
-    SPEC_EINVAL = 1,   /* bad size, stride, temperature, null pointer, small workspace */
+    SPEC_EINVAL = 1,   /* bad size, stride, temperature, null pointer, small or misaligned workspace */
     SPEC_EDTYPE = 2,   /* unknown dtype code */
     SPEC_EALIGN = 3,   /* a logit base pointer not aligned to its element size */
     SPEC_ELAUNCH = 4   /* the HIP runtime refused a kernel launch */
@@ -60,7 +60,9 @@ typedef enum {
  * Bytes of device workspace one call needs for batch b, block length K and
  * vocabulary V (sampling != 0 for spec_sample_accept).  Returns 0 when the
  * sizes are out of range (b < 1, K < 1, K > SPEC_MAX_K, V < 1) or the dtype
- * is unknown.  The workspace needs no initialisation; 256-byte alignment.
+ * is unknown.  The workspace needs no initialisation and must be 256-byte
+ * aligned (every entry point returns SPEC_EINVAL for a smaller or misaligned
+ * workspace).
  */
 size_t spec_workspace_bytes(int b, int K, int V, int dtype, int sampling);
 
@@ -68,10 +70,10 @@ size_t spec_workspace_bytes(int b, int K, int V, int dtype, int sampling);
 const char *spec_status_string(int status);
 
 /*
- * Greedy accept ("greedy-correct by construction": the committed tokens are
- * the target's own argmax chain, identical to plain greedy decoding up to
- * exact ties -- "mlx-dspark 0.0.1" sdist diff, README "How it works";
- * benchmark.py's plain greedy token is argmax of the raw logits).
+ * Greedy accept: the committed tokens are the target's own argmax chain, so
+ * the output equals plain greedy decoding up to exact ties ("mlx-dspark
+ * 0.0.1" sdist diff, README "How it works"; benchmark.py's plain greedy token
+ * is the argmax of the raw logits).
  *
  * For each sequence s: A_i = lowest index of the largest raw logit of target
  * row i (i = 0..K); n = length of the longest prefix with x_i == A_i;
@@ -288,12 +290,14 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
  *                   table's entries for vocabulary entry v
  *   temperatures    double [b]: 0 greedy, > 0 sampling, else tokens -1
  *   seeds           uint64 [b]
- *   hidden          bf16 [b, K, D] and conf_w bf16 [D + r], or NULL (no confidence)
+ *   hidden          bf16 [b, K, D] and conf_w bf16 [D + r]; needed when confidence
+ *                   or lengths is given (else SPEC_EINVAL), unused otherwise
  *   tokens          int32 [b, K] out; -1 from a position whose previous token
  *                   or logits are invalid on
  *   draft_logits    float32 [b, K, V] out (the corrected q_i), 16-byte aligned,
  *                   strides multiples of 4
- *   confidence      float [b, K] out or NULL; lengths int32 [b] out or NULL
+ *   confidence      float [b, K] out or NULL; lengths int32 [b] out or NULL; the
+ *                   confidence head runs when either is given
  *   workspace       spec_markov_workspace_bytes(b, K, V, r) bytes, 256-byte aligned
  * Two kernels per position (the correction on the matrix cores with the base
  * logits added, q_i stored and per-tile records; then per sequence the merge

@@ -1194,7 +1194,7 @@ int spec_greedy_accept(const void *target, int dtype, int64_t t_batch_stride, in
     if (!make_layout(b, K, V, dtype, kCallGreedy, L)) return SPEC_EINVAL;
     if (!target || !draft_tokens || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0) return SPEC_EINVAL;
-    if (workspace_bytes < L.total) return SPEC_EINVAL;
+    if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
     if ((uintptr_t)target % elem_bytes(dtype) != 0) return SPEC_EALIGN;
     Ctx c = {};
     c.target = target;
@@ -1221,7 +1221,7 @@ int spec_sample_accept(const void *target, const void *draft, int dtype, int64_t
     if (!target || !draft || !draft_tokens || !seeds || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
     if (!(temperature > 0.0) || !(temperature < INFINITY)) return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0 || d_row_stride < V || d_batch_stride < 0) return SPEC_EINVAL;
-    if (workspace_bytes < L.total) return SPEC_EINVAL;
+    if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
     const int es = elem_bytes(dtype);
     if ((uintptr_t)target % es != 0 || (uintptr_t)draft % es != 0) return SPEC_EALIGN;
     Ctx c = {};
@@ -1255,7 +1255,7 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t 
     if (!target || !draft || !draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace)
         return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0 || d_row_stride < V || d_batch_stride < 0) return SPEC_EINVAL;
-    if (workspace_bytes < L.total) return SPEC_EINVAL;
+    if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
     const int es = elem_bytes(dtype);
     if ((uintptr_t)target % es != 0 || (uintptr_t)draft % es != 0) return SPEC_EALIGN;
     Ctx c = {};
@@ -1443,7 +1443,7 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
     if (!make_sharded_layout(G, shard_V, b, K, dtype, S)) return SPEC_EINVAL;
     if (!target_shards || !draft_shards || !t_strides || !d_strides) return SPEC_EINVAL;
     if (!draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace) return SPEC_EINVAL;
-    if (workspace_bytes < S.total) return SPEC_EINVAL;
+    if (workspace_bytes < S.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
     const int es = elem_bytes(dtype);
     char *ws = (char *)workspace;
     Ctx cg[kMaxShards];
@@ -1529,7 +1529,9 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
     if (base_row_stride < V || base_batch_stride < 0 || q_row_stride < V || q_batch_stride < 0) return SPEC_EINVAL;
     if (!(threshold == threshold) || !(conf_b == conf_b)) return SPEC_EINVAL;
-    const bool want_conf = confidence != nullptr;
+    // The confidence head runs when either of its outputs is asked for, and
+    // then needs its inputs.
+    const bool want_conf = confidence != nullptr || lengths != nullptr;
     if (want_conf && (!hidden || !conf_w || D < 1 || h_row_stride < D || h_batch_stride < 0)) return SPEC_EINVAL;
     if ((uintptr_t)base % 4) return SPEC_EALIGN;
     if ((uintptr_t)draft_logits % 16 || q_row_stride % 4 || q_batch_stride % 4) return SPEC_EALIGN;

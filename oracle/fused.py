@@ -82,24 +82,47 @@ def abs_products(hidden: np.ndarray, weight: np.ndarray, seqs=None) -> np.ndarra
     return out.reshape(len(idx), K1, V)
 
 
+def lm_head_logits_and_abs(hidden: np.ndarray, weight: np.ndarray, cap: float, seqs=None):
+    """lm_head_logits and abs_products in one pass over the weight (each
+    slab widened once): the same two float64 arrays."""
+    b, K1, D = hidden.shape
+    V = weight.shape[0]
+    idx = np.arange(b) if seqs is None else np.asarray(seqs)
+    H = _widen(np.ascontiguousarray(hidden[idx])).reshape(-1, D)
+    Ha = np.abs(H)
+    out = np.empty((H.shape[0], V), np.float64)
+    absout = np.empty((H.shape[0], V), np.float64)
+    for v0 in range(0, V, _SLAB):
+        v1 = min(V, v0 + _SLAB)
+        Wt = _widen(weight[v0:v1]).T
+        out[:, v0:v1] = H @ Wt
+        np.abs(Wt, out=Wt)
+        absout[:, v0:v1] = Ha @ Wt
+    return softcap(out, cap).reshape(len(idx), K1, V), absout.reshape(len(idx), K1, V)
+
+
 def gamma(n: int) -> float:
     """gamma_n = n u / (1 - n u) for float32 (u = 2^-24)."""
     return n * U32 / (1.0 - n * U32)
 
 
 def fused_mixed_accept(hidden, weight, cap, draft, draft_tokens, temperatures, seeds,
-                       draft_lengths=None, seqs=None) -> dict:
+                       draft_lengths=None, seqs=None, with_abs: bool = False) -> dict:
     """Mixed-rule accept on the lm_head logits rounded to float32.
 
     With `seqs`, only those sequences' logits are formed; the other target
     rows are left at zero and their results are meaningless (the accept of a
     sequence reads only its own rows, and Philox rows stay the batch
     indices).  Returns the C oracle's result dict plus 'logits64' and
-    'logits32' of the formed sequences ([len(seqs), K+1, V])."""
+    'logits32' of the formed sequences ([len(seqs), K+1, V]), and with
+    `with_abs` also 'abs_products' (abs_products of the same sequences)."""
     b, K1, D = hidden.shape
     V = weight.shape[0]
     idx = np.arange(b) if seqs is None else np.asarray(seqs)
-    z64 = lm_head_logits(hidden, weight, cap, idx)
+    if with_abs:
+        z64, absp = lm_head_logits_and_abs(hidden, weight, cap, idx)
+    else:
+        z64, absp = lm_head_logits(hidden, weight, cap, idx), None
     z32 = z64.astype(np.float32)
     target = np.zeros((b, K1, V), np.float32)
     target[idx] = z32
@@ -107,5 +130,7 @@ def fused_mixed_accept(hidden, weight, cap, draft, draft_tokens, temperatures, s
                         temperatures, seeds, draft_lengths)
     res["logits64"] = z64
     res["logits32"] = z32
+    if absp is not None:
+        res["abs_products"] = absp
     res["seqs"] = idx
     return res

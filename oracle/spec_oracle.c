@@ -52,6 +52,12 @@
  *   ORACLE_MUTANT=3  bonus drawn from p_K instead of p_{K+1}
  *   ORACLE_MUTANT=4  greedy ties go to the last maximal index
  *   ORACLE_MUTANT=5  temperature applied to the target side only
+ *   ORACLE_MUTANT=6  zero residual mass draws from the block's last row
+ *                    p_{Ks+1} instead of p_n
+ *   ORACLE_MUTANT=7  zero residual mass has no fallback (the draw finds no
+ *                    token)
+ *   ORACLE_MUTANT=8  the rounding fallback takes the FIRST entry of positive
+ *                    weight instead of the last
  */
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
@@ -409,11 +415,20 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     for (int v = 0; v < V; ++v) {
         R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
     }
+    int weight_row = draw_row;     /* the row whose log-normaliser the weights use */
+#if ORACLE_MUTANT == 7
+    if (0) {
+#else
     if (residual && R == 0.0) {
+#endif
         residual = 0;              /* no residual mass: draw from p_n */
+#if ORACLE_MUTANT == 6
+        weight_row = Ks;
+        toff = (int64_t)s * t_batch_stride + (int64_t)Ks * t_row_stride;
+#endif
         R = 0.0;
         for (int v = 0; v < V; ++v) {
-            R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, 0);
+            R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[weight_row], Cdn, 0);
         }
     }
     double u2 = oracle_uniform(seeds[s], (uint32_t)s, (uint32_t)n, 1u);
@@ -421,9 +436,13 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     int32_t y = -1, last_positive = -1;
     double F = 0.0;
     for (int v = 0; v < V; ++v) {
-        double w = draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
+        double w = draw_weight(target, draft, dtype, toff, doff, v, T, Ct[weight_row], Cdn, residual);
         F += w;
+#if ORACLE_MUTANT == 8
+        if (w > 0.0 && last_positive < 0) {
+#else
         if (w > 0.0) {
+#endif
             last_positive = v;
         }
         if (F > t) {

@@ -54,7 +54,7 @@ def test_status_strings(lib):
 
 def _greedy(lib, **kw):
     a = dict(target=16, dtype=1, bs=8 * 100, rs=100, tok=16, b=2, K=7, V=100, n=16, tokens=16,
-             am=None, ws=16, wsb=1 << 20, stream=None)
+             am=None, ws=256, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.spec_greedy_accept(a["target"], a["dtype"], a["bs"], a["rs"], a["tok"], a["b"], a["K"],
                                   a["V"], a["n"], a["tokens"], a["am"], a["ws"], a["wsb"], a["stream"])
@@ -73,13 +73,14 @@ def test_greedy_argument_validation(lib):
     assert _greedy(lib, rs=99) == 1
     assert _greedy(lib, bs=-1) == 1
     assert _greedy(lib, wsb=16) == 1
+    assert _greedy(lib, ws=256 + 16) == 1    # workspace not 256-byte aligned
     assert _greedy(lib, dtype=7) == 2
     assert _greedy(lib, target=17) == 3      # not aligned to a bf16 element
 
 
 def _sample(lib, **kw):
     a = dict(target=16, draft=16, dtype=1, tbs=800, trs=100, dbs=700, drs=100, tok=16, b=2, K=7, V=100,
-             T=1.0, seeds=16, n=16, tokens=16, p=None, q=None, ws=16, wsb=1 << 20, stream=None)
+             T=1.0, seeds=16, n=16, tokens=16, p=None, q=None, ws=256, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.spec_sample_accept(a["target"], a["draft"], a["dtype"], a["tbs"], a["trs"], a["dbs"],
                                   a["drs"], a["tok"], a["b"], a["K"], a["V"], a["T"], a["seeds"], a["n"],
@@ -95,13 +96,14 @@ def test_sample_argument_validation(lib):
     assert _sample(lib, T=float("nan")) == 1
     assert _sample(lib, drs=50) == 1
     assert _sample(lib, wsb=100) == 1
+    assert _sample(lib, ws=512 + 64) == 1
     assert _sample(lib, dtype=3) == 2
     assert _sample(lib, draft=18, dtype=0) == 3   # fp32 needs 4-byte alignment
 
 
 def _mixed(lib, **kw):
     a = dict(target=16, draft=16, dtype=1, tbs=800, trs=100, dbs=700, drs=100, tok=16, b=2, K=7, V=100,
-             temps=16, lens=None, seeds=16, n=16, tokens=16, p=None, q=None, am=None, ws=16, wsb=1 << 20,
+             temps=16, lens=None, seeds=16, n=16, tokens=16, p=None, q=None, am=None, ws=256, wsb=1 << 20,
              stream=None)
     a.update(kw)
     return lib.spec_mixed_accept(a["target"], a["draft"], a["dtype"], a["tbs"], a["trs"], a["dbs"],
@@ -118,6 +120,7 @@ def test_mixed_argument_validation(lib):
     assert _mixed(lib, lens=16, K=33) == 1
     assert _mixed(lib, lens=16, trs=99) == 1
     assert _mixed(lib, lens=16, wsb=64) == 1
+    assert _mixed(lib, ws=1024 + 128) == 1
     assert _mixed(lib, dtype=4) == 2
     assert _mixed(lib, lens=16, target=15) == 3
     need = lib.spec_mixed_workspace_bytes(2, 7, 100, 1)
@@ -187,10 +190,39 @@ def test_sharded_argument_validation(lib):
     assert call(a1=None) == 1
     assert call(a10=None) == 1                   # temperatures
     assert call(a19=64) == 1                     # workspace too small
+    assert call(a18=4096 + 16) == 1              # workspace not 256-byte aligned
     short = (ctypes.c_int64 * 6)(8 * 1000, 999, 8 * 2000, 2000, 8 * 17, 17)
     assert call(a4=short) == 1                   # row stride below the shard width
     odd = (ctypes.c_void_p * 3)(257, 512, 768)
     assert call(a1=odd) == 3                     # bf16 shard not 2-byte aligned
+
+
+def _markov(lib, **kw):
+    a = dict(base=1024, bbs=7 * 1000, brs=1000, anchors=16, w1=2048, w1rs=256, w2=4096, w2rs=256, r=256,
+             b=2, K=7, V=1000, temps=16, seeds=16, hidden=8192, hbs=7 * 64, hrs=64, D=64, conf_w=16384,
+             conf_b=1.0, thr=0.5, tokens=16, q=32768, qbs=7 * 1000, qrs=1000, conf=16, lens=16, ws=4096,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_markov_block_decode(
+        a["base"], a["bbs"], a["brs"], a["anchors"], a["w1"], a["w1rs"], a["w2"], a["w2rs"], a["r"], a["b"],
+        a["K"], a["V"], a["temps"], a["seeds"], a["hidden"], a["hbs"], a["hrs"], a["D"], a["conf_w"],
+        a["conf_b"], a["thr"], a["tokens"], a["q"], a["qbs"], a["qrs"], a["conf"], a["lens"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+def test_markov_argument_validation(lib):
+    assert lib.spec_markov_workspace_bytes(2, 7, 1000, 96) == 0        # rank not a multiple of 64
+    assert _markov(lib, r=96) == 1
+    assert _markov(lib, ws=4096 + 16) == 1                              # workspace not 256-byte aligned
+    assert _markov(lib, wsb=64) == 1
+    assert _markov(lib, thr=float("nan")) == 1
+    # the confidence head runs when confidence OR lengths is asked for, and
+    # then needs hidden and conf_w: lengths alone without them is rejected
+    assert _markov(lib, conf=None, hidden=None) == 1
+    assert _markov(lib, conf=None, conf_w=None) == 1
+    assert _markov(lib, lens=None, hidden=None) == 1
+    assert _markov(lib, w1=2050) == 3                                   # table not 16-byte aligned
+    assert _markov(lib, q=32772) == 3                                   # q not 16-byte aligned
 
 
 def test_stream_copy_validation(lib):

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
 from parity import (Report, compare_greedy, compare_mixed, compare_sample, run_gpu_greedy,
                     run_gpu_mixed, run_gpu_sample, to_device, seeds_to_device)
@@ -220,6 +221,28 @@ def test_extreme_temperatures_and_masked_vocab(dtype):
     committed = committed[committed >= 0]
     assert not ((committed >= 1000) & (committed < 9000)).any()
     _check(compare_mixed(case, temps, *out, f"extreme_masked_{dtype}"), f"extreme_masked_{dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_residual_mass_draws_from_p_n(dtype):
+    """Identical target and draft rows with the draft token masked in both at
+    slot j_s = s mod (K+1): that slot is rejected with zero residual mass and
+    the token comes from p_{j_s} (the branch that falls back to the target
+    row), through the sampling call and the mixed call (every third sequence
+    greedy there).  V spans several segments with a ragged tail."""
+    case = W.make_zero_mass_case("zmass", b=24, K=5, V=20011, dtype=dtype, T=0.9, seed=17)
+    slot = case.meta["slot"]
+    n, tok, p, q = run_gpu_sample(case)
+    assert (n == slot).all(), (n, slot)
+    res = oracle.sample_accept(case.target, case.draft, case.draft_tokens, case.T, case.seeds)
+    assert (res["residual"] == 0).all()              # the oracle also drew from p_n
+    zt = W.as_f32(case.target)
+    for s in range(case.b):                          # the drawn token has p > 0
+        assert np.isfinite(zt[s, slot[s], tok[s, slot[s]]])
+    rep = compare_sample(case, n, tok, p, q, f"zero_mass_sample_{dtype}", res=res)
+    temps = np.where(np.arange(case.b) % 3 == 0, 0.0, case.T)
+    rep.merge(compare_mixed(case, temps, *run_gpu_mixed(case, temps), f"zero_mass_mixed_{dtype}"))
+    _check(rep, f"zero_residual_mass_{dtype}")
 
 
 def test_mixed_matches_single_rule_calls():

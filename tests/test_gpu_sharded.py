@@ -144,3 +144,17 @@ def test_sharded_seeded_sweep(k):
     for a, r in zip((out[0], out[1], out[4]), (ref[0], ref[1], ref[4])):
         np.testing.assert_array_equal(a, r)
 
+
+
+def test_sharded_zero_residual_mass():
+    """The zero-residual-mass fallback through the sharded call: every shard's
+    residual mass is zero, so the shard selection falls back to the target
+    masses of slot n.  Integer results equal the unsharded call's."""
+    case = W.make_zero_mass_case("zmass_sh", b=18, K=5, V=20011, dtype="bf16", T=0.9, seed=19)
+    temps = np.where(np.arange(case.b) % 4 == 3, 0.0, case.T)
+    widths = [7001, 9000, 4010]
+    out = _run(case, temps, widths)
+    ref = _run_unsharded(case, temps)
+    for a, b_ in zip((out[0], out[1], out[4]), (ref[0], ref[1], ref[4])):
+        np.testing.assert_array_equal(a, b_)
+    _check(compare_mixed(case, temps, *out, "sharded_zero_mass"), "sharded_zero_mass")

@@ -1,8 +1,8 @@
 """Pins of the oracle's greedy accept.
 
-Greedy accept is fixed by the pages as "greedy-correct by construction":
-the committed tokens are the target's own argmax chain, identical to plain
-greedy decoding ("mlx-dspark 0.0.1" sdist diff, README "How it works";
+The pages fix greedy accept by its result: the committed tokens are the
+target's own argmax chain, so the output equals plain greedy decoding
+("mlx-dspark 0.0.1" sdist diff, README "How it works";
 benchmark.py takes the plain greedy token as argmax of the raw logits).  The
 block convention ([K+1, V], row K the bonus position) is the one of
 "dspark-mlx 0.1.0", dspark_mlx/adapter.py.  Pinned against numpy.argmax

@@ -248,6 +248,29 @@ def config(cid: int, b: Optional[int] = None, V: Optional[int] = None) -> Case:
     raise ValueError(f"unknown workload {cid}")
 
 
+
+def make_zero_mass_case(name: str, *, b: int, K: int, V: int, dtype: str = "bf16",
+                        T: float = 0.9, seed: int = 0) -> Case:
+    """A batch whose draws hit zero residual mass.  Every draft block is
+    bitwise its target's first K rows, so every accept ratio is exactly 1;
+    sequence s then masks (-inf, in the target and the draft row alike) its
+    draft token at slot j_s = s mod (K+1) when j_s < K.  That slot has
+    p(x) = 0 and is rejected, and max(0, p - q) is zero over the whole row, so
+    the token is drawn from p_{j_s}; sequences with j_s = K accept every slot
+    and draw the bonus.  meta["slot"] holds j_s."""
+    case = make_case(name, b=b, K=K, V=V, dtype=dtype, target_scale=2.0, draft_sigma=0.5,
+                     T=T, seed=seed, equal_draft_rows=range(b))
+    ninf = np.uint16(0xFF80) if case.target.dtype == np.uint16 else np.float32(-np.inf)
+    slot = np.arange(b) % (K + 1)
+    for s in range(b):
+        j = int(slot[s])
+        if j < K:
+            x = int(case.draft_tokens[s, j])
+            case.target[s, j, x] = ninf
+            case.draft[s, j, x] = ninf
+    case.meta["slot"] = slot
+    return case
+
 # ---------------------------------------------------------------------------
 # Fused verify inputs: the verify forward's final hidden states and the
 # lm_head weight instead of a materialised target logit block.

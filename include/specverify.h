@@ -45,7 +45,8 @@ typedef enum {
     SPEC_EINVAL = 1,   /* bad size, stride, temperature, null pointer, small or misaligned workspace */
     SPEC_EDTYPE = 2,   /* unknown dtype code */
     SPEC_EALIGN = 3,   /* a logit base pointer not aligned to its element size */
-    SPEC_ELAUNCH = 4   /* the HIP runtime refused a kernel launch */
+    SPEC_ELAUNCH = 4,  /* the HIP runtime refused a kernel launch */
+    SPEC_ESCRATCH = 5  /* spec_mixed_accept_noalloc: the call needs more than SPEC_SCRATCH_BYTES */
 } spec_status;
 
 typedef enum {
@@ -170,6 +171,35 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype,
                       int32_t *n_accepted, int32_t *tokens,
                       float *p_draft, float *q_draft, int32_t *target_argmax,
                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * spec_mixed_accept for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as
+ * spec_mixed_accept, without the workspace: the call runs in a fixed array
+ * of SPEC_SCRATCH_BYTES in device memory that the library holds on each GPU
+ * it runs on until the process ends (its address is looked up once per
+ * device, on the first call there).  The call allocates nothing.
+ *
+ * Limit: spec_mixed_workspace_bytes(b, K, V, dtype) must not exceed
+ * SPEC_SCRATCH_BYTES, else SPEC_ESCRATCH before anything is enqueued (8 MiB
+ * holds b = 128 at K = 7, V = 262144 in bf16 or in fp32).  Every call on one
+ * GPU uses the same array: calls that may overlap on one GPU (several
+ * streams, several host threads) race and must be ordered by the caller, for
+ * example on one stream.  The array keeps the last call's contents; no call
+ * needs it cleared.
+ */
+#define SPEC_SCRATCH_BYTES (8u << 20)
+
+int spec_mixed_accept_noalloc(const void *target, const void *draft, int dtype,
+                              int64_t t_batch_stride, int64_t t_row_stride,
+                              int64_t d_batch_stride, int64_t d_row_stride,
+                              const int32_t *draft_tokens, int b, int K, int V,
+                              const double *temperatures, const int32_t *draft_lengths,
+                              const uint64_t *seeds,
+                              int32_t *n_accepted, int32_t *tokens,
+                              float *p_draft, float *q_draft, int32_t *target_argmax,
+                              void *hip_stream);
 
 /*
  * Fused verify: the target logit block is formed inside the call from the

@@ -24,6 +24,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_accept",
+           "mixed_accept_noalloc", "SCRATCH_BYTES",
            "fused_mixed_accept", "lm_head_logits", "fused_workspace_bytes",
            "sharded_mixed_accept", "sharded_workspace_bytes",
            "DraftBlock", "markov_block_decode", "markov_workspace_bytes",
@@ -36,6 +37,7 @@ _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 SPEC_F32 = 0
 SPEC_BF16 = 1
 SPEC_MAX_K = 32
+SCRATCH_BYTES = 8 << 20        # SPEC_SCRATCH_BYTES: the fixed device scratch of mixed_accept_noalloc
 
 
 class SpecError(RuntimeError):
@@ -68,6 +70,9 @@ def _load():
     lib.spec_mixed_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_mixed_accept.restype = i32
+    lib.spec_mixed_accept_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_mixed_accept_noalloc.restype = i32
     f32 = ctypes.c_float
     lib.spec_fused_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_fused_workspace_bytes.restype = sz
@@ -275,6 +280,52 @@ def mixed_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.
         out.q_draft.data_ptr() if out.q_draft is not None else None,
         out.argmax.data_ptr() if out.argmax is not None else None,
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(rc)
+    return out
+
+
+def mixed_accept_noalloc(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                         temperatures: torch.Tensor, seeds: torch.Tensor, *,
+                         draft_lengths: Optional[torch.Tensor] = None, out: Optional[AcceptResult] = None,
+                         stream=None) -> AcceptResult:
+    """mixed_accept without a workspace: the C entry point runs in the
+    library's fixed device scratch (SCRATCH_BYTES per GPU) and allocates
+    nothing; pass `out` to keep this wrapper from allocating the results.
+    Calls that overlap on one GPU race on that scratch."""
+    _on_gpu(target, draft, draft_tokens, temperatures, seeds)
+    if target.dim() != 3 or draft.dim() != 3 or target.stride(2) != 1 or draft.stride(2) != 1:
+        raise ValueError("target [b, K+1, V] and draft [b, K, V] need V contiguous")
+    b, K1, V = target.shape
+    K = K1 - 1
+    if draft.shape != (b, K, V) or draft.dtype != target.dtype:
+        raise ValueError("draft must be [b, K, V] with the target's dtype")
+    if draft_tokens.shape != (b, K) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [b, K] tensor")
+    if temperatures.shape != (b,) or temperatures.dtype != torch.float64 or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be a contiguous float64 [b] tensor")
+    if seeds.shape != (b,) or seeds.element_size() != 8 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous 64-bit [b] tensor")
+    if draft_lengths is not None:
+        _on_gpu(draft_lengths)
+        if (draft_lengths.shape != (b,) or draft_lengths.dtype != torch.int32
+                or not draft_lengths.is_contiguous()):
+            raise ValueError("draft_lengths must be a contiguous int32 [b] tensor")
+    dev = target.device
+    if out is None:
+        out = AcceptResult(torch.empty(b, dtype=torch.int32, device=dev),
+                           torch.empty(b, K1, dtype=torch.int32, device=dev),
+                           p_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           q_draft=torch.empty(b, K, dtype=torch.float32, device=dev),
+                           argmax=torch.empty(b, K1, dtype=torch.int32, device=dev))
+    rc = _lib.spec_mixed_accept_noalloc(
+        target.data_ptr(), draft.data_ptr(), _dtype_code(target), target.stride(0), target.stride(1),
+        draft.stride(0), draft.stride(1), draft_tokens.data_ptr(), b, K, V, temperatures.data_ptr(),
+        draft_lengths.data_ptr() if draft_lengths is not None else None,
+        seeds.data_ptr(), out.n_accepted.data_ptr(), out.tokens.data_ptr(),
+        out.p_draft.data_ptr() if out.p_draft is not None else None,
+        out.q_draft.data_ptr() if out.q_draft is not None else None,
+        out.argmax.data_ptr() if out.argmax is not None else None,
+        _stream_handle(dev, stream))
     _check(rc)
     return out
 

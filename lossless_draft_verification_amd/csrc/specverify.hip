@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "specverify.h"
@@ -1154,6 +1155,57 @@ bool bf16_operand_ok(const void *p, int64_t stride, int D) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch for callers that cannot allocate (code under graph
+// capture, tight serving loops): spec_mixed_accept_noalloc runs the mixed
+// call's kernels with this array as their workspace.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) unsigned char scratch[SPEC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices] = {};
+std::mutex g_scratch_mu;
+
+// The copy of `scratch` on the GPU that `st` runs on (the current device for
+// the null stream), looked up once per device with that device current and
+// kept.  SPEC_ELAUNCH if the runtime cannot give it.
+int scratch_address(hipStream_t st, void **out) {
+    int dev = 0;
+    const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+        (void)hipGetLastError();
+        return SPEC_ELAUNCH;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) {
+                (void)hipGetLastError();
+                return SPEC_ELAUNCH;
+            }
+            const hipError_t se = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev) (void)hipSetDevice(cur);
+            if (se != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return SPEC_ELAUNCH;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SPEC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t spec_workspace_bytes(int b, int K, int V, int dtype, int sampling) {
@@ -1175,6 +1227,7 @@ const char *spec_status_string(int status) {
         case SPEC_EDTYPE: return "unknown dtype";
         case SPEC_EALIGN: return "logit pointer not aligned to its element size";
         case SPEC_ELAUNCH: return "kernel launch failed";
+        case SPEC_ESCRATCH: return "the call needs more than the SPEC_SCRATCH_BYTES of fixed device scratch";
         default: return "unknown status";
     }
 }
@@ -1243,19 +1296,26 @@ int spec_sample_accept(const void *target, const void *draft, int dtype, int64_t
     return dispatch(c, b, workspace, dtype, kCallSample, L, (hipStream_t)hip_stream);
 }
 
-int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
-                      int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
-                      const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
-                      const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, float *p_draft,
-                      float *q_draft, int32_t *target_argmax, void *workspace, size_t workspace_bytes,
-                      void *hip_stream) {
+// Argument checks of the mixed call, shared by its two entry points (the
+// workspace is checked by each).
+static int mixed_check(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
+                       int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
+                       const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
+                       const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, Layout &L) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
-    Layout L;
     if (!make_layout(b, K, V, dtype, kCallMixed, L)) return SPEC_EINVAL;
-    if (!target || !draft || !draft_tokens || !temperatures || !seeds || !n_accepted || !tokens || !workspace)
+    if (!target || !draft || !draft_tokens || !temperatures || !seeds || !n_accepted || !tokens)
         return SPEC_EINVAL;
     if (t_row_stride < V || t_batch_stride < 0 || d_row_stride < V || d_batch_stride < 0) return SPEC_EINVAL;
-    if (workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
+    return SPEC_OK;
+}
+
+static int mixed_run(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
+                     int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
+                     const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
+                     const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens,
+                     float *p_draft, float *q_draft, int32_t *target_argmax, void *workspace, const Layout &L,
+                     void *hip_stream) {
     const int es = elem_bytes(dtype);
     if ((uintptr_t)target % es != 0 || (uintptr_t)draft % es != 0) return SPEC_EALIGN;
     Ctx c = {};
@@ -1277,6 +1337,43 @@ int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t 
     c.q_out = q_draft;
     c.am = target_argmax;
     return dispatch(c, b, workspace, dtype, kCallMixed, L, (hipStream_t)hip_stream);
+}
+
+int spec_mixed_accept(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
+                      int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
+                      const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
+                      const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted, int32_t *tokens, float *p_draft,
+                      float *q_draft, int32_t *target_argmax, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+    Layout L;
+    int rc = mixed_check(target, draft, dtype, t_batch_stride, t_row_stride, d_batch_stride, d_row_stride,
+                         draft_tokens, b, K, V, temperatures, seeds, n_accepted, tokens, L);
+    if (rc != SPEC_OK) return rc;
+    if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0) return SPEC_EINVAL;
+    return mixed_run(target, draft, dtype, t_batch_stride, t_row_stride, d_batch_stride, d_row_stride, draft_tokens,
+                     b, K, V, temperatures, draft_lengths, seeds, n_accepted, tokens, p_draft, q_draft,
+                     target_argmax, workspace, L, hip_stream);
+}
+
+int spec_mixed_accept_noalloc(const void *target, const void *draft, int dtype, int64_t t_batch_stride,
+                              int64_t t_row_stride, int64_t d_batch_stride, int64_t d_row_stride,
+                              const int32_t *draft_tokens, int b, int K, int V, const double *temperatures,
+                              const int32_t *draft_lengths, const uint64_t *seeds, int32_t *n_accepted,
+                              int32_t *tokens, float *p_draft, float *q_draft, int32_t *target_argmax,
+                              void *hip_stream) {
+    Layout L;
+    int rc = mixed_check(target, draft, dtype, t_batch_stride, t_row_stride, d_batch_stride, d_row_stride,
+                         draft_tokens, b, K, V, temperatures, seeds, n_accepted, tokens, L);
+    if (rc != SPEC_OK) return rc;
+    if (L.total > (size_t)SPEC_SCRATCH_BYTES) return SPEC_ESCRATCH;
+    void *ws = nullptr;
+    rc = scratch_address((hipStream_t)hip_stream, &ws);
+    if (rc != SPEC_OK) return rc;
+    // The mixed kernels need no cleared workspace: every record they read in a
+    // call is written earlier in the same call.
+    return mixed_run(target, draft, dtype, t_batch_stride, t_row_stride, d_batch_stride, d_row_stride, draft_tokens,
+                     b, K, V, temperatures, draft_lengths, seeds, n_accepted, tokens, p_draft, q_draft,
+                     target_argmax, ws, L, hip_stream);
 }
 
 int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream) {

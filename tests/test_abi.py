@@ -127,6 +127,35 @@ def test_mixed_argument_validation(lib):
     assert need >= lib.spec_workspace_bytes(2, 7, 100, 1, 1) > 0
 
 
+def test_mixed_noalloc_argument_validation(lib):
+    """The allocation-free mixed call checks its arguments like the workspace
+    call, then refuses a call whose workspace would exceed the fixed device
+    scratch (SPEC_ESCRATCH = 5) before anything is enqueued."""
+    import lossless_draft_verification_amd as L
+
+    def call(**kw):
+        a = dict(target=16, draft=16, dtype=1, tbs=800, trs=100, dbs=700, drs=100, tok=16, b=2, K=7, V=100,
+                 temps=16, lens=None, seeds=16, n=16, tokens=16, p=None, q=None, am=None, stream=None)
+        a.update(kw)
+        return lib.spec_mixed_accept_noalloc(a["target"], a["draft"], a["dtype"], a["tbs"], a["trs"], a["dbs"],
+                                             a["drs"], a["tok"], a["b"], a["K"], a["V"], a["temps"], a["lens"],
+                                             a["seeds"], a["n"], a["tokens"], a["p"], a["q"], a["am"],
+                                             a["stream"])
+    assert call(temps=None) == 1
+    assert call(K=33) == 1
+    assert call(trs=99) == 1
+    assert call(dtype=4) == 2
+    big = dict(b=1024, K=32, V=262144, tbs=33 * 262144, trs=262144, dbs=32 * 262144, drs=262144)
+    assert lib.spec_mixed_workspace_bytes(1024, 32, 262144, 1) > L.SCRATCH_BYTES
+    assert call(**big) == 5
+    assert lib.spec_status_string(5)
+    m = re.search(r"#define SPEC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SCRATCH_BYTES
+    # the workloads' largest call fits: b=128, K=7, V=262144 in bf16 and fp32
+    assert lib.spec_mixed_workspace_bytes(128, 7, 262144, 1) <= L.SCRATCH_BYTES
+    assert lib.spec_mixed_workspace_bytes(128, 7, 262144, 0) <= L.SCRATCH_BYTES
+
+
 def _fused(lib, **kw):
     a = dict(h=256, hbs=8 * 128, hrs=128, w=512, wrs=128, D=128, cap=30.0, draft=1024, dbs=7 * 1000,
              drs=1000, tok=16, b=2, K=7, V=1000, temps=16, lens=None, seeds=16, n=16, tokens=16, p=None,

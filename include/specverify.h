@@ -364,6 +364,18 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
 int spec_set_stage_events(void *const *events, int n_events);
 
 /*
+ * Diagnostic (not part of the accept semantics): the uniforms that the
+ * accept test (tag 0) and the draws (tag 1; the Markov draft draws use tag 2)
+ * take, from the library's own device Philox4x32-10, on a grid of counters:
+ * out[r * npos + p] = U(seed, row0 + r, pos0 + p, tag), row and position
+ * wrapping modulo 2^32.  out: device double [nrow * npos], 8-byte aligned.
+ * For checking the device generator against an independent implementation.
+ * Returns SPEC_EINVAL / SPEC_ELAUNCH on error.
+ */
+int spec_philox_uniforms(uint64_t seed, uint32_t row0, int nrow, uint32_t pos0, int npos, uint32_t tag,
+                         double *out, void *hip_stream);
+
+/*
  * Plain device copy of nbytes (a multiple of 16, 16-byte aligned pointers)
  * with the same 16-byte load path as the row pass, enqueued on hip_stream.
  * Used to calibrate hardware byte counters and to measure the achievable

@@ -29,10 +29,12 @@ __all__ = ["AcceptResult", "greedy_accept", "speculative_sample_accept", "mixed_
            "sharded_mixed_accept", "sharded_workspace_bytes",
            "DraftBlock", "markov_block_decode", "markov_workspace_bytes",
            "workspace_bytes", "mixed_workspace_bytes",
-           "set_stage_events", "stream_copy", "stream_read", "library_path", "SpecError"]
+           "set_stage_events", "stream_copy", "stream_read", "philox_uniforms", "library_path", "SpecError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+# SPEC_LIBRARY names another build of the same library (the host-sanitizer
+# build of _build.build(sanitize=True)); it must exist like the default one.
+_LIB_PATH = os.environ.get("SPEC_LIBRARY") or os.path.join(_PKG, "libspecverify.so")
 
 SPEC_F32 = 0
 SPEC_BF16 = 1
@@ -97,6 +99,9 @@ def _load():
     lib.spec_stream_copy.restype = i32
     lib.spec_stream_read.argtypes = [vp, sz, vp, vp]
     lib.spec_stream_read.restype = i32
+    lib.spec_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i32, ctypes.c_uint32, i32,
+                                         ctypes.c_uint32, vp, vp]
+    lib.spec_philox_uniforms.restype = i32
     return lib
 
 
@@ -327,6 +332,19 @@ def mixed_accept_noalloc(target: torch.Tensor, draft: torch.Tensor, draft_tokens
         out.argmax.data_ptr() if out.argmax is not None else None,
         _stream_handle(dev, stream))
     _check(rc)
+    return out
+
+
+def philox_uniforms(seed: int, row0: int, nrow: int, pos0: int, npos: int, tag: int, *, device="cuda",
+                    stream=None) -> torch.Tensor:
+    """U(seed, row0 + r, pos0 + p, tag) from the library's device Philox, as a
+    float64 [nrow, npos] tensor (diagnostic: the uniforms the accept test and
+    the draws take)."""
+    dev = torch.device(device)
+    out = torch.empty(nrow, npos, dtype=torch.float64, device=dev)
+    _check(_lib.spec_philox_uniforms(int(seed) & (2 ** 64 - 1), int(row0) & 0xFFFFFFFF, int(nrow),
+                                     int(pos0) & 0xFFFFFFFF, int(npos), int(tag) & 0xFFFFFFFF,
+                                     out.data_ptr(), _stream_handle(dev, stream)))
     return out
 
 

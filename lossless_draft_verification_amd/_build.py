@@ -25,14 +25,44 @@ def hipcc() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+# Host-code sanitizers (CPU checks only; the device code is built as usual):
+# every -fsanitize= applies to the host pass alone.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_LIB = os.path.join(PKG, "libspecverify_san.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a process loading the
+    sanitized library must preload."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    out = subprocess.check_output([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], text=True).strip()
+    if os.path.isabs(out) and os.path.exists(out):
+        return out
+    rt = subprocess.check_output([clang, "-print-runtime-dir"], text=True).strip()
+    return os.path.join(rt, "libclang_rt.asan-x86_64.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False, path: str = "") -> str:
+    """Compile the library (gfx950).  With `sanitize`, a build whose host code
+    carries AddressSanitizer and UndefinedBehaviorSanitizer (-O1 -g), written
+    to libspecverify_san.so (or `path`); load it with asan_runtime() preloaded
+    and SPEC_LIBRARY pointing at it."""
+    out = path or (SAN_LIB if sanitize else LIB)
+    tmp = out + ".tmp"
+    flags = list(HIPCC_FLAGS)
+    if sanitize:
+        flags = [f for f in flags if f != "-O3"] + ["-O1", "-g"] + SANITIZE_FLAGS
+    cmd = [hipcc(), *flags, "-I", INCLUDE, SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

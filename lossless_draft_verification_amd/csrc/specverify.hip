@@ -947,6 +947,19 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(Ctx c) {
 }
 
 // ---------------------------------------------------------------------------
+// The uniforms of the accept and draw steps on a grid of counters, for
+// checking the device Philox against an independent one:
+// out[r * npos + p] = U(seed, row0 + r, pos0 + p, tag), counters wrapping mod 2^32.
+
+__global__ __launch_bounds__(kBlock) void philox_grid_kernel(uint64_t seed, uint32_t row0, int nrow, uint32_t pos0,
+                                                             int npos, uint32_t tag, double *out) {
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k >= (int64_t)nrow * npos) return;
+    const int r = (int)(k / npos), p = (int)(k - (int64_t)r * npos);
+    out[k] = philox_uniform(seed, row0 + (uint32_t)r, pos0 + (uint32_t)p, tag);
+}
+
+// ---------------------------------------------------------------------------
 // Streaming copy used to calibrate byte counters.
 
 __global__ __launch_bounds__(kBlock) void stream_copy_kernel(uint4 *__restrict__ dst, const uint4 *__restrict__ src,
@@ -1385,6 +1398,18 @@ int spec_stream_copy(void *dst, const void *src, size_t nbytes, void *hip_stream
     if (grid > INT_MAX) return SPEC_EINVAL;
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)grid), dim3(kBlock), 0, (hipStream_t)hip_stream,
                        (uint4 *)dst, (const uint4 *)src, nvec);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+int spec_philox_uniforms(uint64_t seed, uint32_t row0, int nrow, uint32_t pos0, int npos, uint32_t tag,
+                         double *out, void *hip_stream) {
+    if (!out || nrow < 0 || npos < 0 || (uintptr_t)out % 8 != 0) return SPEC_EINVAL;
+    const int64_t n = (int64_t)nrow * npos;
+    if (n == 0) return SPEC_OK;
+    const int64_t grid = (n + kBlock - 1) / kBlock;
+    if (grid > INT_MAX) return SPEC_EINVAL;
+    hipLaunchKernelGGL(philox_grid_kernel, dim3((unsigned)grid), dim3(kBlock), 0, (hipStream_t)hip_stream, seed,
+                       row0, nrow, pos0, npos, tag, out);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 

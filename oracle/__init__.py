@@ -27,15 +27,19 @@ F32 = 0
 BF16 = 1
 
 
-def build(path: str = _LIB, mutant: int = 0) -> str:
+def build(path: str = _LIB, mutant: int = 0, sanitize: bool = False) -> str:
     """Compile the oracle with gcc -O2 (single-threaded, no fast-math).
 
     `mutant` > 0 builds a planted-mistake variant (see the header of
     spec_oracle.c) for the tests' negative controls; the default is 0.
+    `sanitize` builds it with AddressSanitizer and UndefinedBehaviorSanitizer
+    (-O1 -g); a process loading that build preloads gcc's libasan.
     """
     tmp = path + ".tmp"
+    opt = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer"] if sanitize else ["-O2"]
     subprocess.check_call(
-        ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", f"-DORACLE_MUTANT={int(mutant)}",
+        ["gcc", *opt, "-std=c11", "-Wall", "-Wextra", f"-DORACLE_MUTANT={int(mutant)}",
          "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
     os.replace(tmp, path)
     return path
@@ -66,6 +70,9 @@ class Oracle:
         lib.oracle_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
                                        ctypes.c_uint32]
         lib.oracle_uniform.restype = dbl
+        lib.oracle_uniform_grid.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i32, ctypes.c_uint32, i32,
+                                            ctypes.c_uint32, vp]
+        lib.oracle_uniform_grid.restype = None
         lib.oracle_greedy_accept.argtypes = [vp, i32, i64, i64, vp, i32, i32, i32, vp, vp, vp]
         lib.oracle_greedy_accept.restype = i32
         lib.oracle_sample_accept.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i32, i32, i32,
@@ -93,6 +100,13 @@ class Oracle:
     def uniform(self, seed: int, row: int, pos: int, tag: int) -> float:
         """U(seed, row, pos, tag) = (word0 >> 8) * 2^-24 of Philox at (pos, row, tag, 0)."""
         return self.lib.oracle_uniform(int(seed), int(row), int(pos), int(tag))
+
+    def uniform_grid(self, seed: int, row0: int, nrow: int, pos0: int, npos: int, tag: int) -> np.ndarray:
+        """U(seed, row0 + r, pos0 + p, tag) as a float64 [nrow, npos] array."""
+        out = np.zeros((nrow, npos), np.float64)
+        self.lib.oracle_uniform_grid(int(seed) & (2 ** 64 - 1), int(row0) & 0xFFFFFFFF, int(nrow),
+                                     int(pos0) & 0xFFFFFFFF, int(npos), int(tag) & 0xFFFFFFFF, _ptr(out))
+        return out
 
     def row_log_normaliser(self, row: np.ndarray, T: float) -> float:
         """C = m + ln sum exp(z/T - m) of one logit row (float32 or bf16 bits)."""
@@ -212,10 +226,11 @@ _default = None
 
 
 def default() -> Oracle:
-    """The regular (non-mutant) oracle build, compiled on first use if absent."""
+    """The regular (non-mutant) oracle build, compiled on first use if absent;
+    SPEC_ORACLE_LIBRARY names another build of it (the sanitizer build)."""
     global _default
     if _default is None:
-        _default = Oracle(_LIB)
+        _default = Oracle(os.environ.get("SPEC_ORACLE_LIBRARY") or _LIB)
     return _default
 
 

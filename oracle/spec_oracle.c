@@ -130,6 +130,19 @@ double oracle_uniform(uint64_t seed, uint32_t row, uint32_t pos, uint32_t tag)
     return (double)(out[0] >> 8) * (1.0 / 16777216.0);
 }
 
+/* The same uniforms on a grid of counters: out[r * npos + p] =
+ * U(seed, row0 + r, pos0 + p, tag), row and position wrapping mod 2^32. */
+void oracle_uniform_grid(uint64_t seed, uint32_t row0, int nrow, uint32_t pos0, int npos,
+                         uint32_t tag, double *out)
+{
+    for (int r = 0; r < nrow; ++r) {
+        for (int p = 0; p < npos; ++p) {
+            out[(int64_t)r * npos + p] = oracle_uniform(seed, row0 + (uint32_t)r,
+                                                        pos0 + (uint32_t)p, tag);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Row validity: a row is usable when it holds no NaN, no +inf and at least  */
 /* one finite value (-inf entries are masked vocabulary and are allowed).    */

@@ -75,3 +75,13 @@ def test_uniformity(orc):
     a = np.array([orc.uniform(9, 0, p, 0) for p in range(2000)])
     b = np.array([orc.uniform(9, 0, p, 1) for p in range(2000)])
     assert abs(np.corrcoef(a, b)[0, 1]) < 0.1
+
+
+def test_uniform_grid_is_the_pointwise_uniform(orc):
+    """The grid form the device comparison uses equals U at every counter,
+    including rows and positions that wrap past 2^32."""
+    g = orc.uniform_grid(2 ** 64 - 5, 2 ** 32 - 3, 6, 2 ** 32 - 4, 9, 1)
+    for r in range(6):
+        for p in range(9):
+            want = orc.uniform(2 ** 64 - 5, (2 ** 32 - 3 + r) % 2 ** 32, (2 ** 32 - 4 + p) % 2 ** 32, 1)
+            assert g[r, p] == want

@@ -171,8 +171,8 @@ def test_fused_argument_validation(lib):
     assert lib.spec_fused_workspace_bytes(2, 7, 1000, 100) == 0          # D not a multiple of 64
     assert lib.spec_fused_workspace_bytes(2, 7, 1000, 0) == 0
     need = lib.spec_fused_workspace_bytes(2, 7, 1000, 128)
-    # fp32 mixed layout + tile records + fp32 logits of every row
-    assert need >= lib.spec_mixed_workspace_bytes(2, 7, 1000, 0) + 2 * 8 * 1024 * 4
+    # fp32 logits of every row (rows padded to 64 entries) + the plain segment partials (16 B each)
+    assert need >= 2 * 8 * 1024 * 4 + 2 * 15 * 1 * 16
     assert _fused(lib, D=96) == 1
     assert _fused(lib, h=None) == 1
     assert _fused(lib, w=None) == 1
@@ -290,3 +290,31 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=300, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_boundary_departures_documented(lib):
+    """The built boundary's departures from the first draft of the header, as
+    documented: the workspace depends on the element size; temperatures are
+    double; dtype is a plain int; SPEC_EALIGN means a pointer not aligned to
+    its element size; V stays below 2^31 - 65536; workspaces are 256-byte
+    aligned.  (Nothing here launches a kernel.)"""
+    hdr = open(HEADER).read()
+    # workspace sized per dtype: fp32 rows span twice the 16 KiB segments of bf16 rows
+    for sampling in (0, 1):
+        bf = lib.spec_workspace_bytes(128, 7, 262144, 1, sampling)
+        f32 = lib.spec_workspace_bytes(128, 7, 262144, 0, sampling)
+        assert f32 > bf > 0
+    # double temperature(s) in the declarations and the binding
+    assert re.search(r"double\s+temperature\b", hdr) and re.search(r"const double \*temperatures", hdr)
+    assert lib.spec_sample_accept.argtypes[11] is ctypes.c_double
+    # dtype is an int parameter; codes 0 and 1 only
+    assert re.search(r"spec_greedy_accept\(const void \*target, int dtype", hdr)
+    assert _greedy(lib, dtype=2) == 2 and _greedy(lib, dtype=-1) == 2
+    # element (not 16-byte) alignment is what SPEC_EALIGN reports
+    assert _greedy(lib, target=17) == 3                  # odd address: not a whole bf16 element
+    assert _sample(lib, dtype=0, target=18) == 3          # 2-byte aligned but not fp32-aligned
+    # V limit
+    assert lib.spec_workspace_bytes(1, 7, 2 ** 31 - 65536, 1, 0) == 0
+    assert lib.spec_workspace_bytes(1, 7, 2 ** 31 - 65537, 1, 0) > 0
+    # 256-byte workspace alignment
+    assert _mixed(lib, ws=256 + 8) == 1

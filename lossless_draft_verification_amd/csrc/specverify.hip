@@ -309,7 +309,13 @@ struct Ctx {
     Partial *part;                     // [b, rps, nseg]
     DrawPlan *plan;                    // [b] or NULL (greedy-only calls)
     double *rmass;                     // [b, nres] or NULL
+    int32_t *rlist;                    // residual work list, or NULL: [0] the count, then the sequences
 };
+
+// The residual work list: the row pass clears the count, each scan whose
+// sequence rejects a slot appends the sequence, and the residual pass maps
+// its workgroups onto the listed sequences only.
+constexpr int kListOff = 64;
 
 __device__ inline double seq_temperature(const Ctx &c, int s) { return c.temps ? c.temps[s] : c.T_uniform; }
 
@@ -430,6 +436,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     const int K1 = K + 1;
     __shared__ float sM[2 * SPEC_MAX_K + 1];
     __shared__ double sS[2 * SPEC_MAX_K + 1];
+    __shared__ double sL[2 * SPEC_MAX_K + 1];
     __shared__ int32_t sA[SPEC_MAX_K + 1];
     __shared__ int32_t sBad;
 
@@ -553,7 +560,17 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         return;
     }
 
-    // Sampling: log-normalisers of the 2K+1 rows.
+    // Sampling.  Wave 0 draws the uniforms first, while the segment records
+    // are still in flight: lane i holds U(seed, s, i, 0), the accept test of
+    // slot i, and U(seed, s, i, 1), the draw if slot i is the one drawn.
+    double u_acc = 0.0, u_draw = 0.0;
+    if (wave == 0 && lane < K1) {
+        const uint64_t seed = c.seeds[s];
+        u_acc = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 0u);
+        u_draw = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 1u);
+    }
+
+    // Log-normalisers of the 2K+1 rows.
     const int R = 2 * K + 1;
     const double c64 = 1.4426950408889634 / T;
     // Row r: M = max of the segment maxima, S = sum of the segment sums
@@ -582,6 +599,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         if (lane == 0) {
             sM[r] = M;
             sS[r] = S;
+            sL[r] = log2(S);
             if (!(S > 0.0) || !(S < INFINITY)) sBad = 1;   // NaN/+inf seen, or no finite entry
         }
     };
@@ -611,7 +629,6 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         }
         return;
     }
-    const uint64_t seed = c.seeds[s];
     bool reject = false;
     if (lane < Ks) {
         const double lp = ((double)zt - (double)sM[lane]) / T - log(sS[lane]);
@@ -620,8 +637,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         if (zt == -INFINITY) r = 0.0;                 // p(x) = 0: never accepted
         else if (zd == -INFINITY) r = INFINITY;       // q(x) = 0 < p(x): always accepted
         else r = exp(lp - lq);
-        const double u = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 0u);
-        reject = !(u < r);                            // u < 1, so u < r == u < min(1, r)
+        reject = !(u_acc < r);                        // u < 1, so u < r == u < min(1, r)
         if (c.p_out) c.p_out[(int64_t)s * K + lane] = (float)exp(lp);
         if (c.q_out) c.q_out[(int64_t)s * K + lane] = (float)exp(lq);
     } else if (lane < K) {                            // slots past the block
@@ -630,22 +646,27 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     }
     const unsigned long long rj = __ballot(reject);
     const int n = rj ? (int)__ffsll((long long)rj) - 1 : Ks;
+    // A rejecting sequence takes its place in the residual work list now, so
+    // the atomic's round trip overlaps the rest.
+    int listed = -1;
+    if (lane == 0 && n < Ks && c.rlist) listed = atomicAdd(c.rlist, 1);
+    const double u2 = __shfl(u_draw, n, kWave);
     if (lane < K1) tok[lane] = lane < n ? x : -1;     // slot n is filled by the draw
     if (lane == 0) {
         c.n_out[s] = n;
         DrawPlan pl;
         pl.mode = n < Ks ? kModeResidual : kModeTarget;
         pl.slot = n;
-        pl.u2 = philox_uniform(seed, (uint32_t)s, (uint32_t)n, 1u);
+        pl.u2 = u2;
         pl.T = T;
         const double St = sS[n];
-        const double Lt = log2(St);
+        const double Lt = sL[n];
         pl.Mt = sM[n];
         pl.St = St;
         pl.Lt_hi = (float)Lt;
         pl.Lt_lo = (float)(Lt - (double)pl.Lt_hi);
         if (n < Ks) {
-            const double Ld = log2(sS[K1 + n]);
+            const double Ld = sL[K1 + n];
             pl.Md = sM[K1 + n];
             pl.Ld_hi = (float)Ld;
             pl.Ld_lo = (float)(Ld - (double)pl.Ld_hi);
@@ -655,6 +676,7 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
             pl.Ld_lo = 0.0f;
         }
         c.plan[s] = pl;
+        if (listed >= 0) c.rlist[kListOff + listed] = s;
     }
 }
 
@@ -689,11 +711,18 @@ __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
     const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
     const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
     double acc = 0.0;
-    if constexpr (VEC) {
+    const int64_t vbase = (int64_t)seg * kResSegVec;
+    if (VEC && vbase + kResSegVec <= (int64_t)V / elems_per_vec(DT)) {
+        // The whole segment lies inside the row (the same for every lane).
+        // Loads and arithmetic sit in one block, so the arithmetic on vector u
+        // waits only for the loads of vector u.
+        const uint4 *ta = (const uint4 *)tp + vbase + lane, *db = (const uint4 *)dp + vbase + lane;
         uint4 a[kResVecPerLane], b[kResVecPerLane];
-        const int64_t vbase = (int64_t)seg * kResSegVec;
-        load_vecs<DT, kResVecPerLane>(tp, vbase, lane, V, a);
-        load_vecs<DT, kResVecPerLane>(dp, vbase, lane, V, b);
+#pragma unroll
+        for (int u = 0; u < kResVecPerLane; ++u) {
+            a[u] = load_stream(ta + u * kWave);
+            b[u] = load_stream(db + u * kWave);
+        }
 #pragma unroll
         for (int u = 0; u < kResVecPerLane; ++u) {
             float w[elems_per_vec(DT)];
@@ -703,6 +732,8 @@ __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
             acc += (double)pairwise_sum<elems_per_vec(DT)>(w);
         }
     } else {
+        // The row's last segment when it is partial, or rows not on 16-byte
+        // boundaries: element by element.
         const int64_t e_begin = (int64_t)seg * rseg_elems(DT);
         const int64_t e_end = min((int64_t)V, e_begin + rseg_elems(DT));
         for (int64_t e = e_begin + lane; e < e_end; e += kWave)
@@ -924,6 +955,7 @@ __device__ inline void row_pass_block(const Ctx &c, int blk, int lane) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
+    if (c.rlist && blockIdx.x == 0 && threadIdx.x == 0) c.rlist[0] = 0;
     row_pass_block<DT, VEC>(c, (int)blockIdx.x, (int)threadIdx.x);
 }
 
@@ -933,12 +965,15 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(Ctx c) {
     scan_seq<DT, kScanBlock / kWave>(c, blockIdx.x);
 }
 
-// Residual pass: one single-wave workgroup per (sequence, residual segment).
+// Residual pass: one single-wave workgroup per (listed sequence, residual
+// segment).  The grid covers every sequence; workgroups past the listed ones
+// come last and return at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void residual_kernel(Ctx c) {
-    const int s = blockIdx.x / c.nres;
-    const int seg = blockIdx.x - s * c.nres;
-    residual_wave<DT, VEC>(c, s, seg, threadIdx.x);
+    const int item = blockIdx.x / c.nres;
+    if (item >= c.rlist[0]) return;
+    const int s = c.rlist[kListOff + item];
+    residual_wave<DT, VEC>(c, s, (int)blockIdx.x - item * c.nres, threadIdx.x);
 }
 
 template <int DT, bool VEC>
@@ -1015,7 +1050,7 @@ enum : int { kCallGreedy = 0, kCallSample = 1, kCallMixed = 2 };
 
 struct Layout {
     int nseg, nres, rps;
-    size_t part_off, plan_off, rmass_off, total;
+    size_t part_off, plan_off, rmass_off, rlist_off, total;
 };
 
 bool make_layout(int b, int K, int V, int dtype, int kind, Layout &L) {
@@ -1029,7 +1064,8 @@ bool make_layout(int b, int K, int V, int dtype, int kind, Layout &L) {
     L.part_off = 0;
     L.plan_off = L.part_off + align256((size_t)b * L.rps * (size_t)L.nseg * sizeof(Partial));
     L.rmass_off = L.plan_off + (draws ? align256((size_t)b * sizeof(DrawPlan)) : 0);
-    L.total = L.rmass_off + (draws ? align256((size_t)b * (size_t)L.nres * sizeof(double)) : 0);
+    L.rlist_off = L.rmass_off + (draws ? align256((size_t)b * (size_t)L.nres * sizeof(double)) : 0);
+    L.total = L.rlist_off + (draws ? align256((size_t)(kListOff + b) * sizeof(int32_t)) : 0);
     return true;
 }
 
@@ -1076,6 +1112,7 @@ int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L
     const bool draws = kind != kCallGreedy;
     c.plan = draws ? (DrawPlan *)(ws + L.plan_off) : nullptr;
     c.rmass = draws ? (double *)(ws + L.rmass_off) : nullptr;
+    c.rlist = draws ? (int32_t *)(ws + L.rlist_off) : nullptr;
     const int es = elem_bytes(dtype);
     bool vec = rows_vector_aligned(c.target, es, c.tbs, c.trs);
     if (kind != kCallGreedy) vec = vec && rows_vector_aligned(c.draft, es, c.dbs, c.drs);
@@ -1506,6 +1543,7 @@ int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t 
     c.part = (Partial *)(ws + L.part_off);
     c.plan = (DrawPlan *)(ws + L.plan_off);
     c.rmass = (double *)(ws + L.rmass_off);
+    c.rlist = (int32_t *)(ws + L.rlist_off);
     const bool vec = rows_vector_aligned(draft, 4, d_batch_stride, d_row_stride);
     return vec ? launch_fused<true>(c, la, b, F, (hipStream_t)hip_stream)
                : launch_fused<false>(c, la, b, F, (hipStream_t)hip_stream);

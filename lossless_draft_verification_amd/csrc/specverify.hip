@@ -384,7 +384,9 @@ __device__ inline void row_wave(const Ctx &c, int s, int i, int seg, int lane, i
         double c64;
         split_scale(T, c_hi, c_lo, c64);
         // Per lane: max, then the sum of exp2 at that max -- pairwise in fp32
-        // inside each 16-byte vector, in double across vectors.
+        // inside each 16-byte vector, in double across vectors.  The lane
+        // sums meet at the wave's max, rescaled by exp2 of the (non-positive)
+        // max difference in fp32 with the split scale, as the elements are.
         float ml = -FLT_MAX;
         double sl = 0.0;
         if constexpr (VEC) {
@@ -414,9 +416,10 @@ __device__ inline void row_wave(const Ctx &c, int s, int i, int seg, int lane, i
             }
         }
         const float mw = wave_max(ml);
+        const float dm = ml - mw;
         out.m = mw;
         out.idx = 0;
-        out.S = wave_sum(sl * exp2(((double)ml - (double)mw) * c64));
+        out.S = wave_sum(sl * (double)__builtin_amdgcn_exp2f(fmaf(dm, c_hi, dm * c_lo)));
     }
     if (lane == 0) c.part[((int64_t)s * c.rps + i) * c.nseg + seg] = out;
 }
@@ -959,6 +962,75 @@ __global__ __launch_bounds__(kWave) void row_pass(Ctx c) {
     row_pass_block<DT, VEC>(c, (int)blockIdx.x, (int)threadIdx.x);
 }
 
+// Row pass of a call with per-sequence draft lengths, over the rows that are
+// part of their sequence's block only (a row past the block costs nothing,
+// where the plain row pass spends a workgroup on it): a fixed grid of waves,
+// wave w taking work items w, w + grid, ...  The rows are
+// listed sequence by sequence (target rows 0..Ks, then, sampling, draft rows
+// 0..Ks-1); item k is segment k % nseg of listed row k / nseg.  Lane l holds
+// the first listed row of sequences l + 64 j, so a wave finds an item's
+// sequence with ballots; the sequences' lengths, rules and temperatures sit
+// in LDS.  Three waves per SIMD, as the plain row pass runs.
+constexpr int kListedSeqPerLane = 4;
+constexpr int kListedMaxB = kWave * kListedSeqPerLane;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave, 3) void row_pass_listed(Ctx c, int b) {
+    __shared__ int32_t sFirst[kListedMaxB], sKs[kListedMaxB], sRule[kListedMaxB];
+    __shared__ double sT[kListedMaxB];
+    const int lane = threadIdx.x;
+    if (c.rlist && blockIdx.x == 0 && lane == 0) c.rlist[0] = 0;
+    int first[kListedSeqPerLane];
+    int total = 0;
+#pragma unroll
+    for (int j = 0; j < kListedSeqPerLane; ++j) {
+        const int s = lane + j * kWave;
+        int rows = 0;
+        if (s < b) {
+            const double T = seq_temperature(c, s);
+            const int Ks = seq_len(c, s);
+            const int rule = seq_rule(c, T, Ks);
+            rows = rule == kRuleInvalid ? 0 : rule == kRuleGreedy ? Ks + 1 : 2 * Ks + 1;
+            sT[s] = T;
+            sKs[s] = Ks;
+            sRule[s] = rule;
+        }
+        int incl = rows;                                // inclusive prefix over the lanes
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        first[j] = total + incl - rows;
+        if (s < b) sFirst[s] = first[j];
+        total += __shfl(incl, kWave - 1, kWave);
+    }
+    __syncthreads();
+    const int nseg = c.nseg;
+    const int items = total * nseg;                    // at most the full grid, checked on the host
+    for (int k = (int)blockIdx.x; k < items; k += (int)gridDim.x) {
+        const int r = __builtin_amdgcn_readfirstlane(k / nseg);
+        const int seg = k - r * nseg;
+        // the item's sequence: the last one whose first listed row is <= r
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kListedSeqPerLane; ++j)
+            cnt += __popcll(__ballot(lane + j * kWave < b && first[j] <= r));
+        const int s = cnt - 1;
+        // LDS reads land in vector registers; the values are the same in
+        // every lane, and saying so keeps the rule's branch uniform.
+        const int Ks = __builtin_amdgcn_readfirstlane(sKs[s]);
+        const int rule = __builtin_amdgcn_readfirstlane(sRule[s]);
+        const int li = r - __builtin_amdgcn_readfirstlane(sFirst[s]);   // listed row of the sequence
+        const int i = __builtin_amdgcn_readfirstlane(li <= Ks ? li : c.K + 1 + (li - Ks - 1));
+        const uint64_t tb = (uint64_t)__double_as_longlong(sT[s]);
+        const double T = __longlong_as_double((long long)(
+            (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tb) |
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tb >> 32)) << 32)));
+        row_wave<DT, VEC>(c, s, i, seg, lane, rule, T);
+    }
+}
+
 // Scan of every sequence of the call: one 1024-thread block per sequence.
 template <int DT>
 __global__ __launch_bounds__(kScanBlock) void scan_kernel(Ctx c) {
@@ -1075,13 +1147,41 @@ bool rows_vector_aligned(const void *p, int es, int64_t bs, int64_t rs) {
 
 #include "lm_head_fused.inc"
 
+int device_cu_count();
+
+// Grid of row_pass_listed<DT, VEC>: four times the waves the device holds at
+// once, so each wave takes a few items (measured fastest against one and two
+// times, where waves live longer, and eight, where each wave's table is built
+// for about one item); 0 if unknown.  Read once per device.
+template <int DT, bool VEC>
+int listed_grid() {
+    static std::atomic<int> cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int g = cached[dev].load(std::memory_order_relaxed);
+        if (g > 0) return g;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, row_pass_listed<DT, VEC>, kWave, 0) != hipSuccess)
+        return 0;
+    const int g = 4 * per_cu * device_cu_count();
+    if (g > 0 && dev < 64) cached[dev].store(g, std::memory_order_relaxed);
+    return g;
+}
+
 template <int DT, bool VEC>
 int launch(const Ctx &c, int b, int kind, const Layout &L, hipStream_t st) {
     const int64_t grid_rows = (int64_t)b * c.rpl * L.nseg;
     const int64_t grid_res = (int64_t)b * L.nres;
     if (grid_rows > INT_MAX || grid_res > INT_MAX) return SPEC_EINVAL;
     stage_mark(0, st);
-    hipLaunchKernelGGL((row_pass<DT, VEC>), dim3((unsigned)grid_rows), dim3(kWave), 0, st, c);
+    const int listed = (c.klen && b <= kListedMaxB) ? listed_grid<DT, VEC>() : 0;
+    if (listed > 0)
+        hipLaunchKernelGGL((row_pass_listed<DT, VEC>), dim3((unsigned)min((int64_t)listed, grid_rows)), dim3(kWave),
+                           0, st, c, b);
+    else
+        hipLaunchKernelGGL((row_pass<DT, VEC>), dim3((unsigned)grid_rows), dim3(kWave), 0, st, c);
     if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
     stage_mark(1, st);
     hipLaunchKernelGGL((scan_kernel<DT>), dim3((unsigned)b), dim3(kScanBlock), 0, st, c);

@@ -317,6 +317,28 @@ def test_ragged_full_lengths_equal_no_lengths():
         np.testing.assert_array_equal(u, v)
 
 
+@pytest.mark.parametrize("V", [4096, 1031])
+def test_ragged_listed_and_plain_row_pass_agree(V):
+    """A call with draft lengths and at most 256 sequences streams only the
+    rows inside each block (the listed row pass); a larger one takes the
+    plain row pass.  A 257-sequence call and its first 256 sequences alone
+    must give the same bits there, and the large call meets the oracle bar.
+    V = 1031 puts rows off 16-byte boundaries (element-wise loads)."""
+    b, K = 257, 4
+    base = W.make_case("raglim", b=b, K=K, V=V, dtype="bf16", target_scale=2.5,
+                       draft_sigma=(0.2, 1.5), T=0.8, seed=55)
+    lens = np.random.default_rng(56).integers(0, K + 1, size=b).astype(np.int32)
+    lens[3] = -1
+    case = _ragged_case(base, lens)
+    temps = np.where(np.arange(b) % 3 == 0, 0.0, 0.8)
+    full = run_gpu_mixed(case, temps, lens=lens)
+    part = run_gpu_mixed(case.take(np.arange(256)), temps[:256], lens=lens[:256])
+    for u, v in zip(full, part):
+        np.testing.assert_array_equal(u[:256], v)
+    assert full[0][3] == -1
+    _check(compare_mixed(case, temps, *full, f"ragged_limit_V{V}", lens=lens), f"ragged_limit_V{V}")
+
+
 def test_workload_c5_ragged():
     """b=128, K=7, V=262144 bf16, mixed rules, draft lengths uniform on 0..7."""
     base = W.config(5)

@@ -135,7 +135,8 @@ def cpu_baseline(case, greedy_idx, sample_idx, budget_s: float):
     }
 
 
-KERNEL_KEYS = {"row_pass": "row_pass", "scan_kernel": "scan", "residual_kernel": "residual_mass",
+KERNEL_KEYS = {"row_pass_listed": "row_pass", "row_pass": "row_pass", "scan_kernel": "scan",
+               "residual_kernel": "residual_mass",
                "draw_kernel": "draw_token", "stream_copy_kernel": "stream_copy",
                "lm_head_dl_kernel": "lm_head_gemm", "markov_stream_kernel": "markov_stream",
                "draft_select_kernel": "draft_select"}
@@ -147,7 +148,7 @@ EXTRA_PMC = [
      "--fused --steps 2 --warmup 1 --no-cpu-baseline --no-reference"),
     ("markov", ("markov_stream", "draft_select"), "markov_b128_V262144_r256",
      "markov_block_decode_b128_V262144_r256.md", "--markov --steps 2 --warmup 1 --no-cpu-baseline"),
-    ("ragged", ("row_pass",), "c5_mixed_ragged", "verify_c5_mixed.md",
+    ("ragged", ("row_pass",), "c5_mixed_ragged", "verify_c5_ragged.md",
      "--ragged --steps 3 --warmup 1 --no-cpu-baseline --no-reference"),
     ("sharded", ("row_pass",), "c5_mixed_sharded8", "verify_c5_vocab_sharded8.md",
      "--sharded 8 --steps 3 --warmup 1 --no-cpu-baseline --no-reference"),
@@ -229,6 +230,7 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
                                  "fetch_scale": f_scale, "write_scale": w_scale, "source_sha256_16": digest}}
         lines.append(f"| {k} | {f_med:.0f} | {w_med:.0f} | {byts:.0f} |")
     lines += ["", "Algorithmic bytes of the row pass per launch: 771751936 (every logit read once).", ""]
+    lines += residual_counter_section(pmc)
     with open(os.path.join(prof, "verify_c5_mixed.md"), "w") as f:
         f.write("\n".join(lines))
     # the fused and Markov paths' kernels, appended to their trace summaries
@@ -263,6 +265,62 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
     return 0
 
 
+# Instruction and cycle counters of the residual pass (two rocprofv3 --pmc
+# passes, at most eight SQ counters each, over residual_kernel only).
+RES_PMC = [
+    ("res_sqA", "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES "
+                "SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD"),
+    ("res_sqB", "SQ_THREAD_CYCLES_VALU SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_INSTS_SMEM SQ_ACTIVE_INST_VMEM "
+                "SQ_ACTIVE_INST_SCA SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_ADD_F32 GRBM_GUI_ACTIVE"),
+]
+
+
+def residual_counter_section(pmc: str) -> list:
+    """Markdown lines for the residual pass's SQ counters (median over the
+    dispatches of each counter, summed over the chip), or [] if the passes
+    are absent."""
+    import csv
+    import statistics
+    vals = {}
+    for prefix, _ in RES_PMC:
+        path = os.path.join(pmc, f"{prefix}_counter_collection.csv")
+        if not os.path.exists(path):
+            return []
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if "residual_kernel" not in r["Kernel_Name"]:
+                continue
+            key = (r["Counter_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (name, _), v in per.items():
+            vals.setdefault(name, []).append(v)
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    g = med.get
+    lines = ["## Residual pass: instruction and cycle counters (rocprofv3 --pmc), median per dispatch", "",
+             "Commands (two passes; at most eight SQ counters fit in one):", ""]
+    for prefix, ctrs in RES_PMC:
+        lines += [f"    rocprofv3 --pmc {ctrs} \\",
+                  f"        --kernel-include-regex residual_kernel -d $OUT/pmc -o {prefix} --output-format csv \\",
+                  "        -- python3 $R/bench.py --steps 3 --warmup 1 --settle 0 --no-cpu-baseline --no-reference"]
+    lines += ["", "| counter | value |", "|---|---|"]
+    for k in sorted(med):
+        lines.append(f"| {k} | {med[k]:.0f} |")
+    pairs = 59 * 262144                      # element pairs of the 59 rejected row pairs of c5
+    if g("SQ_INSTS_VALU") and g("SQ_WAVE_CYCLES"):
+        lines += ["", "Derived (c5 rejects 59 row pairs of 262144 entries: 15.47M element pairs):", "",
+                  f"- VALU instructions per element pair (wave instructions x 64 lanes / pairs): "
+                  f"{g('SQ_INSTS_VALU') * 64 / pairs:.1f}, of which transcendental "
+                  f"{g('SQ_INSTS_VALU_TRANS_F32', 0) * 64 / pairs:.2f}",
+                  f"- share of resident wave-cycles issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES): "
+                  f"{g('SQ_ACTIVE_INST_VALU', 0) / g('SQ_WAVE_CYCLES'):.2f}",
+                  f"- share waiting on any instruction's dependency (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES): "
+                  f"{g('SQ_WAIT_INST_ANY', 0) / g('SQ_WAVE_CYCLES'):.2f}",
+                  f"- VALU issue cycles per SIMD (4 per wave64 instruction, 1024 SIMDs): "
+                  f"{g('SQ_INSTS_VALU') * 4 / 1024:.0f}, that is "
+                  f"{g('SQ_INSTS_VALU') * 4 / 1024 / 2.4e3:.2f} us at 2.4 GHz"]
+    return lines + [""]
+
+
 TRACE_SUMMARIES = [
     # (trace dir, -o prefix, profile file, title, workload text, bench arguments)
     ("prof_fused", "fused", "lm_head_fused_verify_b128_V262144_D3840.md",
@@ -276,6 +334,12 @@ TRACE_SUMMARIES = [
      "sequences 0..63 greedy, 64..127 sampled at T=0.8; one spec_markov_block_decode call per step "
      "(7 positions: the streaming correction kernel and the per-sequence select kernel each).",
      "--markov --steps 30 --warmup 3 --no-cpu-baseline"),
+    ("prof_ragged", "ragged", "verify_c5_ragged.md",
+     "Kernel durations: verify step with per-sequence draft lengths",
+     "workload c5 (b=128, K=7, V=262144, bf16, 64 greedy + 64 sampled) with draft lengths drawn uniformly "
+     "from 0..7, one spec_mixed_accept call per step (the listed row pass streams only rows inside each "
+     "block).",
+     "--ragged --steps 200 --warmup 200 --no-cpu-baseline --no-reference"),
     ("prof_sharded", "sharded", "verify_c5_vocab_sharded8.md",
      "Kernel durations: vocabulary-sharded verify, 8 shards",
      "workload c5 (b=128, K=7, V=262144, bf16, 64 greedy + 64 sampled) with the vocabulary in 8 shards of "

@@ -439,7 +439,8 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     const int K1 = K + 1;
     __shared__ float sM[2 * SPEC_MAX_K + 1];
     __shared__ double sS[2 * SPEC_MAX_K + 1];
-    __shared__ double sL[2 * SPEC_MAX_K + 1];
+    __shared__ double sL[2 * SPEC_MAX_K + 1];     // log2 S (the draw's normaliser)
+    __shared__ double sLn[2 * SPEC_MAX_K + 1];    // ln S (p(x), q(x) and the accept ratio)
     __shared__ int32_t sA[SPEC_MAX_K + 1];
     __shared__ int32_t sBad;
 
@@ -598,12 +599,14 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
             const Partial p = pr[j];
             acc += p.S * exp2(((double)p.m - (double)M) * c64);
         }
-        const double S = wave_sum(acc);
+        const double S = wave_sum(acc);                 // the same bits in every lane
         if (lane == 0) {
             sM[r] = M;
             sS[r] = S;
             sL[r] = log2(S);
             if (!(S > 0.0) || !(S < INFINITY)) sBad = 1;   // NaN/+inf seen, or no finite entry
+        } else if (lane == 1) {
+            sLn[r] = log(S);
         }
     };
 #pragma unroll
@@ -634,8 +637,8 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     }
     bool reject = false;
     if (lane < Ks) {
-        const double lp = ((double)zt - (double)sM[lane]) / T - log(sS[lane]);
-        const double lq = ((double)zd - (double)sM[K1 + lane]) / T - log(sS[K1 + lane]);
+        const double lp = ((double)zt - (double)sM[lane]) / T - sLn[lane];
+        const double lq = ((double)zd - (double)sM[K1 + lane]) / T - sLn[K1 + lane];
         double r;
         if (zt == -INFINITY) r = 0.0;                 // p(x) = 0: never accepted
         else if (zd == -INFINITY) r = INFINITY;       // q(x) = 0 < p(x): always accepted
@@ -850,8 +853,14 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
     int nsg = resid ? nres : nseg;
     int per = (nsg + kBlock - 1) / kBlock;
     int j0 = min(nsg, t * per), j1 = min(nsg, j0 + per);
-    double local = 0.0, excl, incl, total;
-    for (int j = j0; j < j1; ++j) local += (resid && j == r0) ? rm_first : seg_mass(j);
+    // The thread's first mass is kept for (b), so the common case (one
+    // segment per thread) reads no mass twice.
+    double local = 0.0, m_first = 0.0, excl, incl, total;
+    for (int j = j0; j < j1; ++j) {
+        const double mj = (resid && j == r0) ? rm_first : seg_mass(j);
+        if (j == j0) m_first = mj;
+        local += mj;
+    }
     block_scan(local, excl, incl, total, sw);
     if (!sharded && resid && !(total > 0.0)) {         // zero residual mass: draw from p_n
         resid = false;
@@ -860,7 +869,11 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
         j0 = min(nsg, t * per);
         j1 = min(nsg, j0 + per);
         local = 0.0;
-        for (int j = j0; j < j1; ++j) local += seg_mass(j);
+        for (int j = j0; j < j1; ++j) {
+            const double mj = seg_mass(j);
+            if (j == j0) m_first = mj;
+            local += mj;
+        }
         block_scan(local, excl, incl, total, sw);
     }
     // u2 < 1: tt < total when total > 0.  A shard draws at the mass the shard
@@ -879,7 +892,7 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
         int sel = -1, last = -1;
         double sel_off = 0.0, last_off = 0.0;
         for (int j = j0; j < j1; ++j) {
-            const double mj = seg_mass(j);
+            const double mj = j == j0 ? m_first : seg_mass(j);
             if (mj > 0.0) {
                 last = j;
                 last_off = run;
@@ -946,9 +959,10 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
 // starts as soon as one wave's resources free up.)
 template <int DT, bool VEC>
 __device__ inline void row_pass_block(const Ctx &c, int blk, int lane) {
-    const int row = blk / c.nseg;
+    // (the same in every lane: scalar loads and pointer arithmetic follow)
+    const int row = __builtin_amdgcn_readfirstlane(blk / c.nseg);
     const int seg = blk - row * c.nseg;
-    const int s = row / c.rpl, i = c.row_lo + (row - s * c.rpl);
+    const int s = __builtin_amdgcn_readfirstlane(row / c.rpl), i = c.row_lo + (row - s * c.rpl);
     const double T = seq_temperature(c, s);
     const int Ks = seq_len(c, s);
     const int rule = seq_rule(c, T, Ks);

@@ -339,6 +339,25 @@ def test_ragged_listed_and_plain_row_pass_agree(V):
     _check(compare_mixed(case, temps, *full, f"ragged_limit_V{V}", lens=lens), f"ragged_limit_V{V}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_draft_tokens_on_segment_edges(dtype):
+    """Draft tokens at the first and last entries of row-pass segments, of
+    16-byte vectors and of the row (V = 65537 leaves a partial last vector):
+    each must give the oracle's p(x), q(x) and decisions."""
+    b, K, V = 12, 6, 65537
+    case = W.make_case("edges", b=b, K=K, V=V, dtype=dtype, target_scale=1.0, draft_sigma=(0.05, 0.3),
+                       T=1.3, seed=57)
+    seg = 8192 if dtype == "bf16" else 4096              # entries per row-pass segment
+    edges = np.array([0, 1, 7, 8, seg - 1, seg, seg + 1, 2 * seg - 1, V - 9, V - 8, V - 2, V - 1], np.int32)
+    x = np.stack([np.roll(edges, -s)[:K] for s in range(b)]).astype(np.int32)
+    import dataclasses
+    case = dataclasses.replace(case, draft_tokens=x)
+    temps = np.full(b, 1.3)
+    temps[::4] = 0.0
+    out = run_gpu_mixed(case, temps)
+    _check(compare_mixed(case, temps, *out, f"segment_edges_{dtype}"), f"segment_edges_{dtype}")
+
+
 def test_workload_c5_ragged():
     """b=128, K=7, V=262144 bf16, mixed rules, draft lengths uniform on 0..7."""
     base = W.config(5)

@@ -16,14 +16,16 @@
 //                  then per lane either max + first argmax (greedy rows) or
 //                  max + sum of
 //                  exp2((z - max) * log2(e)/T) (sampling rows), merged across
-//                  the wave by a butterfly (sums in double).
+//                  the wave by a butterfly (sums in double).  Calls with
+//                  per-sequence draft lengths (up to 256 sequences) take
+//                  row_pass_listed, which streams only rows inside the blocks.
 //   scan           one 1024-thread block per sequence, one wave per row:
 //                  fixed-order merge of the segment partials (double for the
 //                  log-normalisers), then the accept-prefix scan (greedy
 //                  compare, or gather of z[x_i], Philox uniforms and ratio
 //                  test), the outputs and the draw plan for slot n.
 //   residual_mass  one single-wave workgroup per 4 KiB segment of each
-//                  rejected row pair:
+//                  rejected row pair (the sequences the scan listed):
 //                  sum of max(0, p - q) over the segment.
 //   draw_token     one 256-thread block per sampling sequence: block scan over
 //                  the segment masses, re-read of the one segment holding t
@@ -35,10 +37,11 @@
 // (vocab_sharded.inc) runs the verify kernels per shard.
 //
 // Every merge and scan runs in a fixed order with no floating-point atomics,
-// so two calls on the same bytes give the same bits.  Kernel boundaries are
-// the only cross-workgroup synchronisation: a device-scope release fence per
-// workgroup (an L2 write-back on this multi-XCD part) costs far more than a
-// launch.
+// so two calls on the same bytes give the same bits (the one integer atomic,
+// a slot in the residual work list, decides only which workgroup computes a
+// segment).  Kernel boundaries are the only cross-workgroup synchronisation:
+// a device-scope release fence per workgroup (an L2 write-back on this
+// multi-XCD part) costs far more than a launch.
 
 #include <hip/hip_runtime.h>
 

@@ -1193,7 +1193,8 @@ int launch(const Ctx &c, int b, int kind, const Layout &L, hipStream_t st) {
     const int64_t grid_res = (int64_t)b * L.nres;
     if (grid_rows > INT_MAX || grid_res > INT_MAX) return SPEC_EINVAL;
     stage_mark(0, st);
-    const int listed = (c.klen && b <= kListedMaxB) ? listed_grid<DT, VEC>() : 0;
+    int listed = (c.klen && b <= kListedMaxB) ? listed_grid<DT, VEC>() : 0;
+    if (grid_rows > (int64_t)INT_MAX - listed) listed = 0;    // the item loop counts in int
     if (listed > 0)
         hipLaunchKernelGGL((row_pass_listed<DT, VEC>), dim3((unsigned)min((int64_t)listed, grid_rows)), dim3(kWave),
                            0, st, c, b);

@@ -358,6 +358,29 @@ def test_draft_tokens_on_segment_edges(dtype):
     _check(compare_mixed(case, temps, *out, f"segment_edges_{dtype}"), f"segment_edges_{dtype}")
 
 
+@pytest.mark.parametrize("kind", ["all_zero", "all_invalid", "zero_or_invalid"])
+def test_ragged_degenerate_lengths(kind):
+    """256 sequences (the listed row pass) whose blocks hold at most row 0:
+    every length 0 (a plain decode step for each), every length invalid
+    (nothing streamed, every sequence -1), or a mix of the two."""
+    b, K = 256, 3
+    base = W.make_case("ragdeg", b=b, K=K, V=5003, dtype="bf16", target_scale=2.5, draft_sigma=(0.2, 1.5),
+                       rule=np.array([W.GREEDY, W.SAMPLING] * (b // 2)), T=0.9, seed=58)
+    if kind == "all_zero":
+        lens = np.zeros(b, np.int32)
+    elif kind == "all_invalid":
+        lens = np.where(np.arange(b) % 2 == 0, -1, K + 1).astype(np.int32)
+    else:
+        lens = np.where(np.arange(b) % 3 == 0, -2, 0).astype(np.int32)
+    case = _ragged_case(base, lens)
+    temps = np.where(case.rule == W.GREEDY, 0.0, 0.9)
+    out = run_gpu_mixed(case, temps, lens=lens)
+    valid = (lens >= 0) & (lens <= K)
+    assert (out[0][~valid] == -1).all() and (out[0][valid] == 0).all()
+    _check(compare_mixed(case, temps, *out, f"ragged_degenerate_{kind}", lens=lens),
+           f"ragged_degenerate_{kind}")
+
+
 def test_workload_c5_ragged():
     """b=128, K=7, V=262144 bf16, mixed rules, draft lengths uniform on 0..7."""
     base = W.config(5)

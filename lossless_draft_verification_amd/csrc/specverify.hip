@@ -285,6 +285,12 @@ __device__ inline void split_scale(double T, float &c_hi, float &c_lo, double &c
     c_lo = lo < FLT_MIN ? FLT_MIN : lo;
 }
 
+// exp2(d * log2(e)/T) for a non-positive max difference d = m - M (floats),
+// in fp32 with the split scale, as the elements' own weights are taken.
+__device__ inline double rescale_exp2(float d, float c_hi, float c_lo) {
+    return (double)__builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+}
+
 template <int DT>
 __device__ inline const void *row_ptr(const void *base, int64_t bstride, int64_t rstride, int s, int i) {
     return (const char *)base + ((int64_t)s * bstride + (int64_t)i * rstride) * (int64_t)elem_bytes(DT);
@@ -422,7 +428,7 @@ __device__ inline void row_wave(const Ctx &c, int s, int i, int seg, int lane, i
         const float dm = ml - mw;
         out.m = mw;
         out.idx = 0;
-        out.S = wave_sum(sl * (double)__builtin_amdgcn_exp2f(fmaf(dm, c_hi, dm * c_lo)));
+        out.S = wave_sum(sl * rescale_exp2(dm, c_hi, c_lo));
     }
     if (lane == 0) c.part[((int64_t)s * c.rps + i) * c.nseg + seg] = out;
 }
@@ -579,7 +585,9 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
 
     // Log-normalisers of the 2K+1 rows.
     const int R = 2 * K + 1;
-    const double c64 = 1.4426950408889634 / T;
+    float c_hi, c_lo;
+    double c64;
+    split_scale(T, c_hi, c_lo, c64);
     // Row r: M = max of the segment maxima, S = sum of the segment sums
     // rescaled to M (double), the first segment of this lane from `first`.
     auto merge_row = [&](int r, const Partial *first) {
@@ -595,12 +603,12 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
         double acc = 0.0;
         j = lane;
         if (first) {
-            if (j < nseg) acc += first->S * exp2(((double)first->m - (double)M) * c64);
+            if (j < nseg) acc += first->S * rescale_exp2(first->m - M, c_hi, c_lo);
             j += kWave;
         }
         for (; j < nseg; j += kWave) {
             const Partial p = pr[j];
-            acc += p.S * exp2(((double)p.m - (double)M) * c64);
+            acc += p.S * rescale_exp2(p.m - M, c_hi, c_lo);
         }
         const double S = wave_sum(acc);                 // the same bits in every lane
         if (lane == 0) {
@@ -853,7 +861,7 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
 
     // (a) segment masses: thread t sums a contiguous range of segments.
     auto seg_mass = [&](int j) -> double {
-        return resid ? rm[j] : tpart[j].S * exp2(((double)tpart[j].m - (double)pl.Mt) * c64) / pl.St;
+        return resid ? rm[j] : tpart[j].S * rescale_exp2(tpart[j].m - pl.Mt, c_hi, c_lo) / pl.St;
     };
     int nsg = resid ? nres : nseg;
     int per = (nsg + kBlock - 1) / kBlock;

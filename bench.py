@@ -162,14 +162,14 @@ def _short(name: str) -> str:
     return name.split("(")[0][-40:]
 
 
-def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 536870912) -> int:
+def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 536870912, out_dir: str = "") -> int:
     """Turn rocprofv3 CSV output (a kernel trace and --pmc FETCH_SIZE /
     WRITE_SIZE passes over the bench and over --copy-calibration, written
     under `rdir` by the commands listed in the summary) into
     profiles/verify_c5_mixed.md and profiles/traffic.json."""
     import csv
     import statistics
-    prof = os.path.join(ROOT, "profiles")
+    prof = out_dir or os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     tr = os.path.join(rdir, "prof", "mixed_c5_kernel_trace.csv")
     rows = list(csv.DictReader(open(tr)))
@@ -348,7 +348,7 @@ TRACE_SUMMARIES = [
 ]
 
 
-def summarize_traces(rdir: str) -> None:
+def summarize_traces(rdir: str, out_dir: str = "") -> None:
     """profiles/*.md summaries of the kernel traces of the fused, Markov and
     sharded paths (whichever are present under rdir)."""
     import csv
@@ -372,7 +372,7 @@ def summarize_traces(rdir: str) -> None:
             short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+        with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), fname), "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote profiles/{fname}")
 

@@ -65,5 +65,32 @@ def build(verbose: bool = False, sanitize: bool = False, path: str = "") -> str:
     return out
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi_caller.c")
+C_CALLER = os.path.join(ROOT, "tests", "_bin", "c_abi_caller")
+
+
+def rocm_root() -> str:
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    return root if os.path.isdir(os.path.join(root, "include", "hip")) else "/opt/rocm"
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """Compile tests/c_abi_caller.c, a plain C program that calls the
+    library through include/specverify.h and the HIP runtime's C API (gcc,
+    no HIP compiler), against the in-tree libspecverify.so."""
+    rocm = rocm_root()
+    os.makedirs(os.path.dirname(C_CALLER), exist_ok=True)
+    tmp = C_CALLER + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, C_CALLER_SRC, "-o", tmp,
+           "-L", PKG, "-lspecverify", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../lossless_draft_verification_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, C_CALLER)
+    return C_CALLER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

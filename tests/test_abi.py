@@ -318,3 +318,20 @@ def test_boundary_departures_documented(lib):
     assert lib.spec_workspace_bytes(1, 7, 2 ** 31 - 65537, 1, 0) > 0
     # 256-byte workspace alignment
     assert _mixed(lib, ws=256 + 8) == 1
+
+
+def test_plain_c_caller_builds_and_links(tmp_path):
+    """tests/c_abi_caller.c (a C11 program using only include/specverify.h and
+    the HIP runtime's C API, built by build() with gcc) links against the
+    in-tree library and rejects bad input before any HIP call."""
+    import subprocess
+    caller = os.path.join(ROOT, "tests", "_bin", "c_abi_caller")
+    assert os.path.exists(caller), f"{caller} is missing: run __graft_entry__.build()"
+    libs = subprocess.run(["ldd", caller], capture_output=True, text=True, check=True).stdout
+    assert re.search(r"libspecverify\.so => .*lossless_draft_verification_amd/libspecverify\.so", libs), libs
+    usage = subprocess.run([caller], capture_output=True, text=True, timeout=60)
+    assert usage.returncode == 2 and "usage" in usage.stderr
+    bad = tmp_path / "bad.bin"
+    bad.write_bytes(b"\x00" * 20)                    # b = 0: rejected before anything touches a GPU
+    r = subprocess.run([caller, str(bad), str(tmp_path / "out.bin")], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "bad header" in r.stderr

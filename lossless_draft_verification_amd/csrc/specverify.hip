@@ -698,35 +698,78 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
 }
 
 // ---------------------------------------------------------------------------
-// Draw weights.  p(v) = exp2((z - M) * log2(e)/T - log2 S), evaluated as
-// fma(dz, c_hi, -L_hi) + fma(dz, c_lo, -L_lo) so the large terms cancel inside
-// one rounding.  A -inf logit gives -inf in both products (c_hi, c_lo > 0),
-// hence weight 0.  The residual pass and the draw call the same function on
-// the same constants, so a weight has the same bits in both.
+// Draw weights.  p(v) = exp2((z - M) * c - L) with c = log2(e)/T and
+// L = log2 S.  With B = M*c + L the exponent is z*c - B, evaluated as
+// fma(z, c_hi, -B_hi) + fma(z, c_lo, -B_lo) (B split hi + lo like c): each
+// product is exact inside its fma and the large terms cancel inside one
+// rounding, so the exponent carries the error of its last two roundings, as
+// with the difference z - M formed first, in two fewer operations per
+// element.  The low parts' own rounding is 2^-48 |B| absolute, so this
+// folded form is taken while |B| <= 2^20 (below 2^-28); past that (tiny T or
+// huge logits) the exponent is fma(z - M, c_hi, -L_hi) + fma(z - M, c_lo,
+// -L_lo).  A -inf logit gives -inf in both products (c_hi, c_lo > 0), hence
+// weight 0.  The residual pass and the draw build the constants from the same
+// plan with the same code (draw_exp), so a weight has the same bits in both.
+//
+// DrawExp holds the offset subtracted first (M, or 0 in the folded form) and
+// the exponent's constant (L or B).  z - 0 is z, bit for bit, so the general
+// evaluation (FOLDED = false) gives the folded form's bits too: the draw
+// takes it for either form, and only the residual pass, where the two
+// operations per element count, instantiates the folded one.
 
-__device__ inline float target_weight(float zt, const DrawPlan &pl, float c_hi, float c_lo) {
-    const float dz = zt - pl.Mt;
-    return __builtin_amdgcn_exp2f(fmaf(dz, c_hi, -pl.Lt_hi) + fmaf(dz, c_lo, -pl.Lt_lo));
+struct DrawExp {
+    float c_hi, c_lo;
+    float Mt, Et_hi, Et_lo;     // target row: offset (M, or 0 folded) and L or B, split hi + lo
+    float Md, Ed_hi, Ed_lo;     // draft row (residual draws), the same
+    bool fold;                  // the folded form for both rows
+};
+
+__device__ inline bool fold_split(float M, float L_hi, float L_lo, double c64, float &B_hi, float &B_lo) {
+    const double B = (double)M * c64 + ((double)L_hi + (double)L_lo);
+    B_hi = (float)B;
+    B_lo = (float)(B - (double)B_hi);
+    return fabs(B) <= 1048576.0;                    // false for NaN
 }
 
-__device__ inline float residual_weight(float zt, float zd, const DrawPlan &pl, float c_hi, float c_lo) {
-    const float dzd = zd - pl.Md;
-    const float q = __builtin_amdgcn_exp2f(fmaf(dzd, c_hi, -pl.Ld_hi) + fmaf(dzd, c_lo, -pl.Ld_lo));
-    const float w = target_weight(zt, pl, c_hi, c_lo) - q;
+__device__ inline DrawExp draw_exp(const DrawPlan &pl, float c_hi, float c_lo, double c64) {
+    DrawExp x;
+    x.c_hi = c_hi;
+    x.c_lo = c_lo;
+    x.fold = fold_split(pl.Mt, pl.Lt_hi, pl.Lt_lo, c64, x.Et_hi, x.Et_lo) &&
+             fold_split(pl.Md, pl.Ld_hi, pl.Ld_lo, c64, x.Ed_hi, x.Ed_lo);
+    if (x.fold) {
+        x.Mt = 0.0f;
+        x.Md = 0.0f;
+    } else {
+        x.Mt = pl.Mt;
+        x.Md = pl.Md;
+        x.Et_hi = pl.Lt_hi;
+        x.Et_lo = pl.Lt_lo;
+        x.Ed_hi = pl.Ld_hi;
+        x.Ed_lo = pl.Ld_lo;
+    }
+    return x;
+}
+
+// FOLDED = true only where x.fold holds.
+template <bool FOLDED>
+__device__ inline float target_weight(float zt, const DrawExp &x) {
+    const float z = FOLDED ? zt : zt - x.Mt;
+    return __builtin_amdgcn_exp2f(fmaf(z, x.c_hi, -x.Et_hi) + fmaf(z, x.c_lo, -x.Et_lo));
+}
+
+template <bool FOLDED>
+__device__ inline float residual_weight(float zt, float zd, const DrawExp &x) {
+    const float z = FOLDED ? zd : zd - x.Md;
+    const float q = __builtin_amdgcn_exp2f(fmaf(z, x.c_hi, -x.Ed_hi) + fmaf(z, x.c_lo, -x.Ed_lo));
+    const float w = target_weight<FOLDED>(zt, x) - q;
     return w > 0.0f ? w : 0.0f;
 }
 
-// Residual mass of segment `seg` of sequence s's rejected row pair, one wave.
-template <int DT, bool VEC>
-__device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
-    const DrawPlan pl = c.plan[s];
-    if (pl.mode != kModeResidual) return;
-    const int V = c.V;
-    float c_hi, c_lo;
-    double c64;
-    split_scale(pl.T, c_hi, c_lo, c64);
-    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
-    const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
+// Sum of the residual weights of one 4 KiB-per-row segment, this lane's share.
+template <int DT, bool VEC, bool FOLDED>
+__device__ inline double residual_lane_sum(const void *tp, const void *dp, int seg, int V, const DrawExp &x,
+                                           int lane) {
     double acc = 0.0;
     const int64_t vbase = (int64_t)seg * kResSegVec;
     if (VEC && vbase + kResSegVec <= (int64_t)V / elems_per_vec(DT)) {
@@ -747,7 +790,7 @@ __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
             float w[elems_per_vec(DT)];
 #pragma unroll
             for (int k = 0; k < elems_per_vec(DT); ++k)
-                w[k] = residual_weight(vec_elem<DT>(a[u], k), vec_elem<DT>(b[u], k), pl, c_hi, c_lo);
+                w[k] = residual_weight<FOLDED>(vec_elem<DT>(a[u], k), vec_elem<DT>(b[u], k), x);
             acc += (double)pairwise_sum<elems_per_vec(DT)>(w);
         }
     } else {
@@ -756,8 +799,25 @@ __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
         const int64_t e_begin = (int64_t)seg * rseg_elems(DT);
         const int64_t e_end = min((int64_t)V, e_begin + rseg_elems(DT));
         for (int64_t e = e_begin + lane; e < e_end; e += kWave)
-            acc += (double)residual_weight(elem_at<DT>(tp, e), elem_at<DT>(dp, e), pl, c_hi, c_lo);
+            acc += (double)residual_weight<FOLDED>(elem_at<DT>(tp, e), elem_at<DT>(dp, e), x);
     }
+    return acc;
+}
+
+// Residual mass of segment `seg` of sequence s's rejected row pair, one wave.
+template <int DT, bool VEC>
+__device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
+    const DrawPlan pl = c.plan[s];
+    if (pl.mode != kModeResidual) return;
+    const int V = c.V;
+    float c_hi, c_lo;
+    double c64;
+    split_scale(pl.T, c_hi, c_lo, c64);
+    const DrawExp x = draw_exp(pl, c_hi, c_lo, c64);
+    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
+    const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
+    const double acc = x.fold ? residual_lane_sum<DT, VEC, true>(tp, dp, seg, V, x, lane)
+                              : residual_lane_sum<DT, VEC, false>(tp, dp, seg, V, x, lane);
     const double Sw = wave_sum(acc);
     if (lane == 0) c.rmass[(int64_t)s * c.nres + seg] = Sw;
 }
@@ -767,9 +827,8 @@ __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
 // Writes the drawn index to *sY (or the segment's last positive weight to
 // *sLastPos when tl sits at or past the segment's recomputed total).
 template <int DT, bool VEC, int E, bool RESID>
-__device__ inline void search_segment(const void *tp, const void *dp, int64_t e_seg0, int V, const DrawPlan &pl,
-                                      float c_hi, float c_lo, double tl, double *sw, int32_t *sY,
-                                      int32_t *sLastPos) {
+__device__ inline void search_segment(const void *tp, const void *dp, int64_t e_seg0, int V, const DrawExp &x,
+                                      double tl, double *sw, int32_t *sY, int32_t *sLastPos) {
     constexpr int EPV = elems_per_vec(DT);
     const int64_t e0 = e_seg0 + (int64_t)threadIdx.x * E;
     float w[E];
@@ -786,12 +845,12 @@ __device__ inline void search_segment(const void *tp, const void *dp, int64_t e_
             for (int u = 0; u < NV; ++u)
 #pragma unroll
                 for (int k = 0; k < EPV; ++k)
-                    w[u * EPV + k] = residual_weight(vec_elem<DT>(a[u], k), vec_elem<DT>(b[u], k), pl, c_hi, c_lo);
+                    w[u * EPV + k] = residual_weight<false>(vec_elem<DT>(a[u], k), vec_elem<DT>(b[u], k), x);
         } else {
 #pragma unroll
             for (int u = 0; u < NV; ++u)
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) w[u * EPV + k] = target_weight(vec_elem<DT>(a[u], k), pl, c_hi, c_lo);
+                for (int k = 0; k < EPV; ++k) w[u * EPV + k] = target_weight<false>(vec_elem<DT>(a[u], k), x);
         }
     } else {
 #pragma unroll
@@ -799,8 +858,8 @@ __device__ inline void search_segment(const void *tp, const void *dp, int64_t e_
             const int64_t e = e0 + k;
             float wk = 0.0f;
             if (e < V) {
-                if constexpr (RESID) wk = residual_weight(elem_at<DT>(tp, e), elem_at<DT>(dp, e), pl, c_hi, c_lo);
-                else wk = target_weight(elem_at<DT>(tp, e), pl, c_hi, c_lo);
+                if constexpr (RESID) wk = residual_weight<false>(elem_at<DT>(tp, e), elem_at<DT>(dp, e), x);
+                else wk = target_weight<false>(elem_at<DT>(tp, e), x);
             }
             w[k] = wk;
         }
@@ -930,13 +989,14 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
 
     // (c) re-read the segment and search it.
     const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
+    const DrawExp x = draw_exp(pl, c_hi, c_lo, c64);
     if (resid) {
         const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
         search_segment<DT, VEC, (int)(rseg_elems(DT) / kBlock), true>(
-            tp, dp, (int64_t)seg * rseg_elems(DT), V, pl, c_hi, c_lo, tl, sw, &sY, &sLastPos);
+            tp, dp, (int64_t)seg * rseg_elems(DT), V, x, tl, sw, &sY, &sLastPos);
     } else {
         search_segment<DT, VEC, (int)(seg_elems(DT) / kBlock), false>(
-            tp, tp, (int64_t)seg * seg_elems(DT), V, pl, c_hi, c_lo, tl, sw, &sY, &sLastPos);
+            tp, tp, (int64_t)seg * seg_elems(DT), V, x, tl, sw, &sY, &sLastPos);
     }
     __syncthreads();
     if (t == 0) {

@@ -224,6 +224,43 @@ def test_extreme_temperatures_and_masked_vocab(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_exponent_offsets(dtype):
+    """Draws whose exponent offset B = M log2(e)/T + log2 S lies past 2^20,
+    where the draw weights are taken from z - M instead of the folded form:
+    fp32 logits with a common offset of 10^6 at T = 0.5 and 1 (past the
+    bound) next to T = 2 and 3 (inside it), so the two forms meet in one call;
+    bf16 logits at T = 5e-6 and 2e-6 (one-hot softmaxes, past the bound)
+    next to T = 0.8.  Every sampling sequence draws (a residual or a bonus
+    token), and the result must match the oracle as everywhere else."""
+    import dataclasses
+    b, K, V = 12, 4, 20011
+    case = W.make_case("offsets", b=b, K=K, V=V, dtype=dtype, target_scale=2.5,
+                       draft_sigma=(0.2, 1.5), T=1.0, seed=83)
+    if dtype == "f32":
+        t = (case.target.astype(np.float64) + 1.0e6).astype(np.float32)
+        d = (case.draft.astype(np.float64) + 1.0e6).astype(np.float32)
+        case = dataclasses.replace(case, target=t, draft=d)
+        temps = np.array([0.5, 1.0, 2.0, 3.0, 0.0, 0.5, 1.0, 2.0, 0.0, 1.0, 0.5, 3.0])
+    else:
+        temps = np.array([5e-6, 2e-6, 0.8, 5e-6, 0.0, 2e-6, 0.8, 5e-6, 0.0, 2e-6, 5e-6, 0.8])
+    out = run_gpu_mixed(case, temps)
+    assert (out[0] >= 0).all()
+    # Host check that both forms are taken: B of the target row each
+    # sampling sequence draws from (slot n).
+    zt = W.as_f32(case.target).astype(np.float64)
+    past = []
+    for s in np.flatnonzero(temps > 0):
+        n = int(out[0][s])
+        assert out[1][s, n] >= 0
+        z = zt[s, n]
+        c = np.log2(np.e) / temps[s]
+        B = z.max() * c + np.log2(np.exp2((z - z.max()) * c).sum())
+        past.append(abs(B) > 2.0 ** 20)
+    assert any(past) and not all(past), past
+    _check(compare_mixed(case, temps, *out, f"large_offsets_{dtype}"), f"large_offsets_{dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_residual_mass_draws_from_p_n(dtype):
     """Identical target and draft rows with the draft token masked in both at
     slot j_s = s mod (K+1): that slot is rejected with zero residual mass and

@@ -13,10 +13,15 @@ LIB = os.path.join(PKG, "libspecverify.so")
 
 # -ffp-contract=off: the arithmetic is exactly what the source writes (every
 # fused multiply-add is an explicit fmaf).  Packed fp32 instructions are
-# switched off for the device code.
+# switched off for the device code.  The atomic optimizer is off: it turns
+# the scan's one-lane append to the residual work list into a wave-combined
+# atomic whose result is waited for at once, which puts the atomic's round
+# trip on the scan's critical path (without it the wait falls after the
+# draw plan is written).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -318,12 +318,32 @@ struct Ctx {
     Partial *part;                     // [b, rps, nseg]
     DrawPlan *plan;                    // [b] or NULL (greedy-only calls)
     double *rmass;                     // [b, nres] or NULL
-    int32_t *rlist;                    // residual work list, or NULL: [0] the count, then the sequences
+    int32_t *rlist;                    // residual work list, or NULL: [0] the count, then the items
+    uint32_t nres_m, nres_l;           // nres as a multiply-high divisor (fast_div)
 };
 
+// n / d for 0 <= n < 2^31 and d >= 1 by a multiply-high and a shift, all in
+// scalar registers for wave-uniform n (the hardware has no integer divide):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> l (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994;
+// mulhi(n, m) <= n, so the sum stays below 2^32).
+inline void fast_div(uint32_t d, uint32_t &m, uint32_t &l) {
+    l = 0;
+    while (l < 32 && (uint64_t(1) << l) < d) ++l;
+    m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+}
+
+__device__ inline uint32_t fdiv(uint32_t n, uint32_t m, uint32_t l) { return (__umulhi(n, m) + n) >> l; }
+
+inline void set_nres(Ctx &c, int nres) {
+    c.nres = nres;
+    fast_div((uint32_t)(nres > 0 ? nres : 1), c.nres_m, c.nres_l);
+}
+
 // The residual work list: the row pass clears the count, each scan whose
-// sequence rejects a slot appends the sequence, and the residual pass maps
-// its workgroups onto the listed sequences only.
+// sequence rejects a slot appends a work item (ResItem, from int32 kListOff
+// on), and the residual pass maps its workgroups onto the listed items only.
 constexpr int kListOff = 64;
 
 __device__ inline double seq_temperature(const Ctx &c, int s) { return c.temps ? c.temps[s] : c.T_uniform; }
@@ -432,6 +452,100 @@ __device__ inline void row_wave(const Ctx &c, int s, int i, int seg, int lane, i
     }
     if (lane == 0) c.part[((int64_t)s * c.rps + i) * c.nseg + seg] = out;
 }
+
+// ---------------------------------------------------------------------------
+// Draw weight constants.  A draw weight is exp2 of an exponent formed from
+// c = log2(e)/T (split hi + lo), an offset subtracted first and a constant,
+// per row (the weights and the two forms of their exponent are defined with
+// the draw, below).  DrawExp holds the offset (M, or 0 in the folded form)
+// and the constant (L, or B), split hi + lo.  z - 0 is z, bit for bit, so the
+// general evaluation (FOLDED = false) gives the folded form's bits too: the
+// draw takes it for either form, and only the residual pass, where the two
+// operations per element count, instantiates the folded one.
+struct DrawExp {
+    float c_hi, c_lo;
+    float Mt, Et_hi, Et_lo;     // target row: offset (M, or 0 folded) and L or B, split hi + lo
+    float Md, Ed_hi, Ed_lo;     // draft row (residual draws), the same
+    bool fold;                  // the folded form for both rows
+};
+
+__device__ inline bool fold_split(float M, float L_hi, float L_lo, double c64, float &B_hi, float &B_lo) {
+    const double B = (double)M * c64 + ((double)L_hi + (double)L_lo);
+    B_hi = (float)B;
+    B_lo = (float)(B - (double)B_hi);
+    return fabs(B) <= 1048576.0;                    // false for NaN
+}
+
+__device__ inline DrawExp draw_exp(const DrawPlan &pl, float c_hi, float c_lo, double c64) {
+    DrawExp x;
+    x.c_hi = c_hi;
+    x.c_lo = c_lo;
+    x.fold = fold_split(pl.Mt, pl.Lt_hi, pl.Lt_lo, c64, x.Et_hi, x.Et_lo) &&
+             fold_split(pl.Md, pl.Ld_hi, pl.Ld_lo, c64, x.Ed_hi, x.Ed_lo);
+    if (x.fold) {
+        x.Mt = 0.0f;
+        x.Md = 0.0f;
+    } else {
+        x.Mt = pl.Mt;
+        x.Md = pl.Md;
+        x.Et_hi = pl.Lt_hi;
+        x.Et_lo = pl.Lt_lo;
+        x.Ed_hi = pl.Ld_hi;
+        x.Ed_lo = pl.Ld_lo;
+    }
+    return x;
+}
+
+// One residual work item, written by the scan of a rejecting sequence: the
+// sequence, its rejected slot and the weight constants the draw will use
+// (draw_exp of its plan), as 32-bit words, so a residual wave needs one round
+// trip (the count and its item, loaded together) before its row loads.
+struct ResItem {
+    int32_t s, slot;
+    float c_hi, c_lo, Mt, Et_hi, Et_lo, Md, Ed_hi, Ed_lo;
+    int32_t fold, pad;
+};
+
+__device__ inline ResItem res_item(int s, int slot, const DrawExp &x) {
+    ResItem it;
+    it.s = s;
+    it.slot = slot;
+    it.c_hi = x.c_hi;
+    it.c_lo = x.c_lo;
+    it.Mt = x.Mt;
+    it.Et_hi = x.Et_hi;
+    it.Et_lo = x.Et_lo;
+    it.Md = x.Md;
+    it.Ed_hi = x.Ed_hi;
+    it.Ed_lo = x.Ed_lo;
+    it.fold = x.fold ? 1 : 0;
+    it.pad = 0;
+    return it;
+}
+
+__device__ inline DrawExp res_item_exp(const ResItem &it) {
+    DrawExp x;
+    x.c_hi = it.c_hi;
+    x.c_lo = it.c_lo;
+    x.Mt = it.Mt;
+    x.Et_hi = it.Et_hi;
+    x.Et_lo = it.Et_lo;
+    x.Md = it.Md;
+    x.Ed_hi = it.Ed_hi;
+    x.Ed_lo = it.Ed_lo;
+    x.fold = it.fold != 0;
+    return x;
+}
+
+// Every word of the item in a register before the code that follows, so the
+// compiler cannot move the item's loads below the exit test (and wait for
+// them in a second round trip).
+__device__ __forceinline__ void res_item_ready(const ResItem &it) {
+    asm volatile("" ::"s"(it.s), "s"(it.slot), "s"(it.c_hi), "s"(it.c_lo), "s"(it.Mt), "s"(it.Et_hi),
+                 "s"(it.Et_lo), "s"(it.Md), "s"(it.Ed_hi), "s"(it.Ed_lo), "s"(it.fold));
+}
+
+__device__ inline const ResItem *res_items(const Ctx &c) { return (const ResItem *)(c.rlist + kListOff); }
 
 // ---------------------------------------------------------------------------
 // Accept scan of one sequence by one block of NW waves.  Wave w merges rows
@@ -693,7 +807,8 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
             pl.Ld_lo = 0.0f;
         }
         c.plan[s] = pl;
-        if (listed >= 0) c.rlist[kListOff + listed] = s;
+        if (listed >= 0)   // the draw's own constants, bit for bit
+            ((ResItem *)(c.rlist + kListOff))[listed] = res_item(s, n, draw_exp(pl, c_hi, c_lo, c64));
     }
 }
 
@@ -710,46 +825,6 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
 // -L_lo).  A -inf logit gives -inf in both products (c_hi, c_lo > 0), hence
 // weight 0.  The residual pass and the draw build the constants from the same
 // plan with the same code (draw_exp), so a weight has the same bits in both.
-//
-// DrawExp holds the offset subtracted first (M, or 0 in the folded form) and
-// the exponent's constant (L or B).  z - 0 is z, bit for bit, so the general
-// evaluation (FOLDED = false) gives the folded form's bits too: the draw
-// takes it for either form, and only the residual pass, where the two
-// operations per element count, instantiates the folded one.
-
-struct DrawExp {
-    float c_hi, c_lo;
-    float Mt, Et_hi, Et_lo;     // target row: offset (M, or 0 folded) and L or B, split hi + lo
-    float Md, Ed_hi, Ed_lo;     // draft row (residual draws), the same
-    bool fold;                  // the folded form for both rows
-};
-
-__device__ inline bool fold_split(float M, float L_hi, float L_lo, double c64, float &B_hi, float &B_lo) {
-    const double B = (double)M * c64 + ((double)L_hi + (double)L_lo);
-    B_hi = (float)B;
-    B_lo = (float)(B - (double)B_hi);
-    return fabs(B) <= 1048576.0;                    // false for NaN
-}
-
-__device__ inline DrawExp draw_exp(const DrawPlan &pl, float c_hi, float c_lo, double c64) {
-    DrawExp x;
-    x.c_hi = c_hi;
-    x.c_lo = c_lo;
-    x.fold = fold_split(pl.Mt, pl.Lt_hi, pl.Lt_lo, c64, x.Et_hi, x.Et_lo) &&
-             fold_split(pl.Md, pl.Ld_hi, pl.Ld_lo, c64, x.Ed_hi, x.Ed_lo);
-    if (x.fold) {
-        x.Mt = 0.0f;
-        x.Md = 0.0f;
-    } else {
-        x.Mt = pl.Mt;
-        x.Md = pl.Md;
-        x.Et_hi = pl.Lt_hi;
-        x.Et_lo = pl.Lt_lo;
-        x.Ed_hi = pl.Ld_hi;
-        x.Ed_lo = pl.Ld_lo;
-    }
-    return x;
-}
 
 // FOLDED = true only where x.fold holds.
 template <bool FOLDED>
@@ -804,22 +879,27 @@ __device__ inline double residual_lane_sum(const void *tp, const void *dp, int s
     return acc;
 }
 
-// Residual mass of segment `seg` of sequence s's rejected row pair, one wave.
+// Residual mass of segment `seg` of sequence s's rejected row pair (slot),
+// one wave.
+template <int DT, bool VEC>
+__device__ inline void residual_seg(const Ctx &c, int s, int slot, const DrawExp &x, int seg, int lane) {
+    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, slot);
+    const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, slot);
+    const double acc = x.fold ? residual_lane_sum<DT, VEC, true>(tp, dp, seg, c.V, x, lane)
+                              : residual_lane_sum<DT, VEC, false>(tp, dp, seg, c.V, x, lane);
+    const double Sw = wave_sum(acc);
+    if (lane == 0) c.rmass[(int64_t)s * c.nres + seg] = Sw;
+}
+
+// The same from sequence s's plan (the vocabulary-sharded residual pass).
 template <int DT, bool VEC>
 __device__ inline void residual_wave(const Ctx &c, int s, int seg, int lane) {
     const DrawPlan pl = c.plan[s];
     if (pl.mode != kModeResidual) return;
-    const int V = c.V;
     float c_hi, c_lo;
     double c64;
     split_scale(pl.T, c_hi, c_lo, c64);
-    const DrawExp x = draw_exp(pl, c_hi, c_lo, c64);
-    const void *tp = row_ptr<DT>(c.target, c.tbs, c.trs, s, pl.slot);
-    const void *dp = row_ptr<DT>(c.draft, c.dbs, c.drs, s, pl.slot);
-    const double acc = x.fold ? residual_lane_sum<DT, VEC, true>(tp, dp, seg, V, x, lane)
-                              : residual_lane_sum<DT, VEC, false>(tp, dp, seg, V, x, lane);
-    const double Sw = wave_sum(acc);
-    if (lane == 0) c.rmass[(int64_t)s * c.nres + seg] = Sw;
+    residual_seg<DT, VEC>(c, s, pl.slot, draw_exp(pl, c_hi, c_lo, c64), seg, lane);
 }
 
 // Inverse-CDF search inside one segment [e_seg0, e_seg0 + 256*E) of the
@@ -1129,10 +1209,14 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(Ctx c) {
 // come last and return at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void residual_kernel(Ctx c) {
-    const int item = blockIdx.x / c.nres;
-    if (item >= c.rlist[0]) return;
-    const int s = c.rlist[kListOff + item];
-    residual_wave<DT, VEC>(c, s, (int)blockIdx.x - item * c.nres, threadIdx.x);
+    const int item = (int)fdiv(blockIdx.x, c.nres_m, c.nres_l);
+    // The count and the item are read together (item < b: inside the list;
+    // past the count it holds stale bytes, never used).
+    const int count = c.rlist[0];
+    const ResItem it = res_items(c)[item];
+    res_item_ready(it);
+    if (item >= count) return;
+    residual_seg<DT, VEC>(c, it.s, it.slot, res_item_exp(it), (int)blockIdx.x - item * c.nres, threadIdx.x);
 }
 
 template <int DT, bool VEC>
@@ -1224,7 +1308,7 @@ bool make_layout(int b, int K, int V, int dtype, int kind, Layout &L) {
     L.plan_off = L.part_off + align256((size_t)b * L.rps * (size_t)L.nseg * sizeof(Partial));
     L.rmass_off = L.plan_off + (draws ? align256((size_t)b * sizeof(DrawPlan)) : 0);
     L.rlist_off = L.rmass_off + (draws ? align256((size_t)b * (size_t)L.nres * sizeof(double)) : 0);
-    L.total = L.rlist_off + (draws ? align256((size_t)(kListOff + b) * sizeof(int32_t)) : 0);
+    L.total = L.rlist_off + (draws ? align256(kListOff * sizeof(int32_t) + (size_t)b * sizeof(ResItem)) : 0);
     return true;
 }
 
@@ -1289,7 +1373,7 @@ int launch(const Ctx &c, int b, int kind, const Layout &L, hipStream_t st) {
 int dispatch(Ctx c, int b, void *workspace, int dtype, int kind, const Layout &L, hipStream_t st) {
     char *ws = (char *)workspace;
     c.nseg = L.nseg;
-    c.nres = L.nres;
+    set_nres(c, L.nres);
     c.rps = L.rps;
     c.row_lo = 0;
     c.rpl = L.rps;
@@ -1721,7 +1805,7 @@ int spec_fused_mixed_accept(const void *hidden, int64_t h_batch_stride, int64_t 
     c.am = target_argmax;
     const Layout &L = F.L;
     c.nseg = L.nseg;
-    c.nres = L.nres;
+    set_nres(c, L.nres);
     c.rps = L.rps;
     c.row_lo = 0;
     c.rpl = L.rps;
@@ -1814,7 +1898,7 @@ int spec_sharded_mixed_accept(int G, const void *const *target_shards, const voi
         c.K = K;
         c.V = shard_V[g];
         c.nseg = S.nseg[g];
-        c.nres = S.nres[g];
+        set_nres(c, S.nres[g]);
         c.rps = S.rps;
         c.row_lo = 0;
         c.rpl = S.rps;
@@ -1900,7 +1984,7 @@ int spec_markov_block_decode(const float *base, int64_t base_batch_stride, int64
     c.K = K - 1;                         // q has K rows per sequence, tokens [b, K]
     c.V = V;
     c.nseg = L.nseg;
-    c.nres = 0;
+    set_nres(c, 0);
     c.rps = K;
     c.row_lo = 0;
     c.rpl = K;

@@ -223,6 +223,18 @@ def test_extreme_temperatures_and_masked_vocab(dtype):
     _check(compare_mixed(case, temps, *out, f"extreme_masked_{dtype}"), f"extreme_masked_{dtype}")
 
 
+def test_residual_work_beyond_the_resident_waves():
+    """More residual work than the chip holds waves at once: 96 sampling
+    sequences with drafts far from the target (nearly every block rejects) at
+    V=262144 bf16, 128 residual segments per rejected row pair, so the
+    residual pass's waves stride over more than one segment each."""
+    case = W.make_case("res_stride", b=96, K=3, V=262144, dtype="bf16", target_scale=3.0,
+                       draft_sigma=2.5, T=1.0, seed=91)
+    n, tok, p, q = run_gpu_sample(case)
+    assert int((n < case.K).sum()) * 128 > 256 * 32, n
+    _check(compare_sample(case, n, tok, p, q, "res_stride"), "res_stride")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_large_exponent_offsets(dtype):
     """Draws whose exponent offset B = M log2(e)/T + log2 S lies past 2^20,

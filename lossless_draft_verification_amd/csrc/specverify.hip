@@ -547,6 +547,19 @@ __device__ __forceinline__ void res_item_ready(const ResItem &it) {
 
 __device__ inline const ResItem *res_items(const Ctx &c) { return (const ResItem *)(c.rlist + kListOff); }
 
+// exp(l) of a log-probability l (double, <= 0 or -inf) as a float, in fp32
+// hardware arithmetic: with a = l log2(e) = a_hi + a_lo (a_hi its float
+// rounding, |a_lo| <= 2^-24 |a|), exp2(a_hi) (1 + a_lo ln 2) is within a few
+// float ulps of exp(l) (the dropped term is of order a_lo^2).  Below
+// 2^-200 the float is 0 either way; NaN stays NaN.
+__device__ inline float exp_to_float(double l) {
+    const double a = l * 1.4426950408889634;
+    if (a < -200.0) return 0.0f;
+    const float a_hi = (float)a;
+    const float a_lo = (float)(a - (double)a_hi);
+    return __builtin_amdgcn_exp2f(a_hi) * fmaf(a_lo, 0.69314718f, 1.0f);
+}
+
 // ---------------------------------------------------------------------------
 // Accept scan of one sequence by one block of NW waves.  Wave w merges rows
 // w, w + NW, ... (each wave's first kPre row loads issued together, before
@@ -690,11 +703,13 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     // Sampling.  Wave 0 draws the uniforms first, while the segment records
     // are still in flight: lane i holds U(seed, s, i, 0), the accept test of
     // slot i, and U(seed, s, i, 1), the draw if slot i is the one drawn.
-    double u_acc = 0.0, u_draw = 0.0;
+    // 1/T too, so that after the barrier the log-probabilities take products.
+    double u_acc = 0.0, u_draw = 0.0, inv_T = 0.0;
     if (wave == 0 && lane < K1) {
         const uint64_t seed = c.seeds[s];
         u_acc = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 0u);
         u_draw = philox_uniform(seed, (uint32_t)s, (uint32_t)lane, 1u);
+        inv_T = 1.0 / T;
     }
 
     // Log-normalisers of the 2K+1 rows.
@@ -762,15 +777,15 @@ __device__ inline void scan_seq(const Ctx &c, int s) {
     }
     bool reject = false;
     if (lane < Ks) {
-        const double lp = ((double)zt - (double)sM[lane]) / T - sLn[lane];
-        const double lq = ((double)zd - (double)sM[K1 + lane]) / T - sLn[K1 + lane];
+        const double lp = ((double)zt - (double)sM[lane]) * inv_T - sLn[lane];
+        const double lq = ((double)zd - (double)sM[K1 + lane]) * inv_T - sLn[K1 + lane];
         double r;
         if (zt == -INFINITY) r = 0.0;                 // p(x) = 0: never accepted
         else if (zd == -INFINITY) r = INFINITY;       // q(x) = 0 < p(x): always accepted
         else r = exp(lp - lq);
         reject = !(u_acc < r);                        // u < 1, so u < r == u < min(1, r)
-        if (c.p_out) c.p_out[(int64_t)s * K + lane] = (float)exp(lp);
-        if (c.q_out) c.q_out[(int64_t)s * K + lane] = (float)exp(lq);
+        if (c.p_out) c.p_out[(int64_t)s * K + lane] = exp_to_float(lp);
+        if (c.q_out) c.q_out[(int64_t)s * K + lane] = exp_to_float(lq);
     } else if (lane < K) {                            // slots past the block
         if (c.p_out) c.p_out[(int64_t)s * K + lane] = NAN;
         if (c.q_out) c.q_out[(int64_t)s * K + lane] = NAN;

@@ -1101,6 +1101,14 @@ __device__ inline void draw_core(const Ctx &c, int s, const DrawPlan &pl, const 
     }
 }
 
+// Every field of a plan in registers before the code that follows, so the
+// compiler cannot load the fields after the early-exit tests on the mode and
+// the shard (three dependent round trips instead of one).
+__device__ __forceinline__ void plan_ready(const DrawPlan &pl) {
+    asm volatile("" ::"s"(pl.mode), "s"(pl.slot), "s"(pl.u2), "s"(pl.T), "s"(pl.Mt), "s"(pl.Md), "s"(pl.Lt_hi),
+                 "s"(pl.Lt_lo), "s"(pl.Ld_hi), "s"(pl.Ld_lo), "s"(pl.St), "s"(pl.shard), "s"(pl.t_local));
+}
+
 // The draw of sequence s from the plan and records in the workspace.
 template <int DT, bool VEC>
 __device__ inline void draw_seq(const Ctx &c, int s) {
@@ -1113,6 +1121,7 @@ __device__ inline void draw_seq(const Ctx &c, int s) {
     const int r0 = min(nres, (int)threadIdx.x * rper);
     const double rm_first = r0 < min(nres, r0 + rper) ? rm[r0] : 0.0;
     const DrawPlan pl = c.plan[s];
+    plan_ready(pl);
     draw_core<DT, VEC>(c, s, pl, c.part + ((int64_t)s * c.rps + pl.slot) * c.nseg, rm, rm_first);
 }
 

@@ -23,9 +23,10 @@
 //                  fixed-order merge of the segment partials (double for the
 //                  log-normalisers), then the accept-prefix scan (greedy
 //                  compare, or gather of z[x_i], Philox uniforms and ratio
-//                  test), the outputs and the draw plan for slot n.
+//                  test), the outputs and the draw plan for slot n; a
+//                  rejecting sequence appends a residual work item.
 //   residual_mass  one single-wave workgroup per 4 KiB segment of each
-//                  rejected row pair (the sequences the scan listed):
+//                  rejected row pair (the work items the scans appended):
 //                  sum of max(0, p - q) over the segment.
 //   draw_token     one 256-thread block per sampling sequence: block scan over
 //                  the segment masses, re-read of the one segment holding t
@@ -1228,9 +1229,9 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(Ctx c) {
     scan_seq<DT, kScanBlock / kWave>(c, blockIdx.x);
 }
 
-// Residual pass: one single-wave workgroup per (listed sequence, residual
-// segment).  The grid covers every sequence; workgroups past the listed ones
-// come last and return at once.
+// Residual pass: one single-wave workgroup per (work item, residual
+// segment).  The grid covers every sequence; workgroups past the listed
+// items come last and return at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void residual_kernel(Ctx c) {
     const int item = (int)fdiv(blockIdx.x, c.nres_m, c.nres_l);

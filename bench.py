@@ -259,6 +259,10 @@ def summarize_rocprof(rdir: str, workload: str = "c5_mixed", nbytes_copy: int = 
             sec.append(f"| {k} | {len(fm[k])} | {f_med:.0f} | {w_med:.0f} | {byts:.0f} |")
         with open(os.path.join(prof, fname), "a") as f:
             f.write("\n".join(sec) + "\n")
+    gemm = gemm_counter_section(pmc)
+    if gemm:
+        with open(os.path.join(prof, "lm_head_fused_verify_b128_V262144_D3840.md"), "a") as f:
+            f.write("\n".join(gemm) + "\n")
     with open(os.path.join(prof, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     print("\n".join(lines))
@@ -319,6 +323,58 @@ def residual_counter_section(pmc: str) -> list:
                   f"{g('SQ_INSTS_VALU') * 4 / 1024:.0f}, that is "
                   f"{g('SQ_INSTS_VALU') * 4 / 1024 / 2.4e3:.2f} us at 2.4 GHz"]
     return lines + [""]
+
+
+# Matrix-pipe and clock counters of the fused GEMM (one rocprofv3 --pmc pass
+# over lm_head_dl_kernel), with its dispatches' own timestamps.
+GEMM_PMC = ("gemm_sq", "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES")
+GEMM_FLOPS = 2 * 1024 * 3840 * 262144          # b*(K+1) x D x V, two flops per product
+XCDS, SIMDS, FLOPS_PER_SIMD_CYCLE, NOMINAL_GHZ = 8, 1024, 1024, 2.4
+
+
+def gemm_counter_section(pmc: str) -> list:
+    """Markdown lines for the fused GEMM's SQ/GRBM counters: per dispatch the
+    clock (GRBM_GUI_ACTIVE summed over the XCDs / XCDs / duration) and the
+    matrix pipe's busy share at that clock (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs
+    over clock x duration); medians over the dispatches after the first
+    third (the clock ramps over the first ones).  [] if the pass is absent."""
+    import csv
+    import statistics
+    path = os.path.join(pmc, f"{GEMM_PMC[0]}_counter_collection.csv")
+    if not os.path.exists(path):
+        return []
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if "lm_head_dl_kernel" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [per[k] for k in sorted(per, key=int)]
+    disp = [d for d in disp if d.get("GRBM_GUI_ACTIVE") and d.get("SQ_VALU_MFMA_BUSY_CYCLES") and d["dur"] > 0]
+    if not disp:
+        return []
+    steady = disp[len(disp) // 3:]
+    ghz = [d["GRBM_GUI_ACTIVE"] / XCDS / d["dur"] / 1e9 for d in steady]
+    busy = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / (d["GRBM_GUI_ACTIVE"] / XCDS) for d in steady]
+    dur = [d["dur"] * 1e3 for d in steady]
+    ideal = GEMM_FLOPS / FLOPS_PER_SIMD_CYCLE
+    mfma = statistics.median(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in steady)
+    lines = ["", "## Matrix pipe and clock of the GEMM (rocprofv3 --pmc), dispatches after the first third", "",
+             "Command:", "",
+             f"    rocprofv3 --pmc {GEMM_PMC[1]} --kernel-include-regex lm_head_dl \\",
+             f"        -d $OUT/pmc -o {GEMM_PMC[0]} --output-format csv \\",
+             "        -- python3 $R/bench.py --fused --steps 2 --warmup 1 --settle 0 --no-cpu-baseline --no-reference", "",
+             "| measure | median | range |", "|---|---|---|",
+             f"| duration (ms) | {statistics.median(dur):.3f} | {min(dur):.3f}-{max(dur):.3f} |",
+             f"| clock, GRBM_GUI_ACTIVE / {XCDS} XCDs / duration (GHz) | {statistics.median(ghz):.3f} | "
+             f"{min(ghz):.3f}-{max(ghz):.3f} |",
+             f"| matrix pipe busy at that clock | {statistics.median(busy):.3f} | {min(busy):.3f}-{max(busy):.3f} |",
+             "",
+             f"SQ_VALU_MFMA_BUSY_CYCLES reads {mfma:.0f} per dispatch; the product needs {ideal:.0f} SIMD-cycles "
+             f"of v_mfma_f32_32x32x16_bf16 ({GEMM_FLOPS:.3e} flops at {FLOPS_PER_SIMD_CYCLE} per SIMD-cycle), so the "
+             "counter is the matrix pipe's work itself. The same work at the nominal "
+             f"{NOMINAL_GHZ} GHz is the {NOMINAL_GHZ * FLOPS_PER_SIMD_CYCLE * SIMDS / 1e3:.0f} TFLOP/s bf16 peak.", ""]
+    return lines
 
 
 TRACE_SUMMARIES = [

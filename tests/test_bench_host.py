@@ -91,3 +91,27 @@ def test_summariser_scales_and_records(tmp_path):
     assert ent["bytes_per_launch"] == pytest.approx((1001.0 * 2.0 + 2.0 * 1.0) * 1024.0)
     assert ent["source_sha256_16"] == b.source_digest()
     assert traffic["scan"]["c5_mixed"]["bytes_per_launch"] == pytest.approx((10.0 * 2.0 + 1.0) * 1024.0)
+
+
+def test_gemm_counter_section(tmp_path):
+    """Clock and matrix-pipe share from synthetic GEMM counters: 8 XCDs of
+    1.8e6 GRBM cycles over 1 ms is 1.8 GHz; the ideal MFMA cycles over that
+    clock's 1.8e6 cycles per SIMD give the busy share; the first third of the
+    dispatches (the clock ramp) is left out."""
+    b = _bench()
+    pmc = tmp_path / "pmc"
+    header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    ideal = b.GEMM_FLOPS / b.FLOPS_PER_SIMD_CYCLE
+    rows = []
+    for d in range(6):
+        grbm = (0.9e6 if d < 2 else 1.8e6) * b.XCDS          # the first two: a slow clock
+        for name, val in (("GRBM_GUI_ACTIVE", grbm), ("SQ_VALU_MFMA_BUSY_CYCLES", ideal),
+                          ("SQ_BUSY_CYCLES", 1.0), ("SQ_WAVES", 32768)):
+            rows.append([d, "void lm_head_dl_kernel<0>(LmArgs)", name, val, 0, 1_000_000])
+        rows.append([d, "void row_pass<1, true>(Ctx)", "GRBM_GUI_ACTIVE", 1.0, 0, 1000])
+    _write(str(pmc / "gemm_sq_counter_collection.csv"), header, rows)
+    text = "\n".join(b.gemm_counter_section(str(pmc)))
+    busy = ideal / b.SIMDS / 1.8e6
+    assert "| clock, GRBM_GUI_ACTIVE / 8 XCDs / duration (GHz) | 1.800 | 1.800-1.800 |" in text
+    assert f"| matrix pipe busy at that clock | {busy:.3f} |" in text
+    assert b.gemm_counter_section(str(tmp_path / "absent")) == []

@@ -181,23 +181,39 @@ static int32_t row_argmax(const void *base, int dtype, int64_t off, int V)
     return best;
 }
 
-/* Log-normaliser of softmax(z / T): C = m + ln sum_v exp(z_v / T - m) with
- * m = max_v z_v / T, so that ln p(v) = z_v / T - C. */
-static double row_log_normaliser(const void *base, int dtype, int64_t off,
-                                 int V, double T)
+/* Log-normaliser of softmax(z / T), kept as the pair (M, L) with
+ * M = max_v z_v (the raw logits) and L = ln sum_v exp((z_v - M) / T), so that
+ * ln p(v) = (z_v - M) / T - L.  This is the log-sum-exp of z / T with the
+ * row maximum subtracted before the division: z_v - M is exact in double for
+ * float inputs, where z_v / T - (m + ln S) would lose |z / T| 2^-53 to the
+ * magnitude (1e-4 relative in p at |z / T| = 1e12). */
+typedef struct {
+    double M, L;
+} RowNorm;
+
+static RowNorm row_log_normaliser(const void *base, int dtype, int64_t off,
+                                  int V, double T)
 {
-    double m = -INFINITY;
+    RowNorm n;
+    n.M = -INFINITY;
     for (int v = 0; v < V; ++v) {
-        double a = logit_at(base, dtype, off + v) / T;
-        if (a > m) {
-            m = a;
+        double z = logit_at(base, dtype, off + v);
+        if (z > n.M) {
+            n.M = z;
         }
     }
     double S = 0.0;
     for (int v = 0; v < V; ++v) {
-        S += exp(logit_at(base, dtype, off + v) / T - m);
+        S += exp((logit_at(base, dtype, off + v) - n.M) / T);
     }
-    return m + log(S);
+    n.L = log(S);
+    return n;
+}
+
+/* ln p(v) of logit z under the row's log-normaliser. */
+static double log_prob(double z, RowNorm n, double T)
+{
+    return (z - n.M) / T - n.L;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -286,13 +302,13 @@ int oracle_greedy_accept(const void *target, int dtype,
  * p_{K+1}, or a rejected slot whose residual mass is zero). */
 static double draw_weight(const void *target, const void *draft, int dtype,
                           int64_t t_off, int64_t d_off, int v, double T,
-                          double Ct, double Cd, int residual)
+                          RowNorm Ct, RowNorm Cd, int residual)
 {
-    double p = exp(logit_at(target, dtype, t_off + v) / T - Ct);
+    double p = exp(log_prob(logit_at(target, dtype, t_off + v), Ct, T));
     if (!residual) {
         return p;
     }
-    double q = exp(logit_at(draft, dtype, d_off + v) / T - Cd);
+    double q = exp(log_prob(logit_at(draft, dtype, d_off + v), Cd, T));
 #if ORACLE_MUTANT == 1
     double w = p + 0.0 * q;
 #elif ORACLE_MUTANT == 2
@@ -364,8 +380,8 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     }
 
     /* Step 1: log-normalisers of every target and draft row. */
-    double *Ct = (double *)malloc(sizeof(double) * (size_t)(K + 1));
-    double *Cd = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    RowNorm *Ct = (RowNorm *)malloc(sizeof(RowNorm) * (size_t)(K + 1));
+    RowNorm *Cd = (RowNorm *)malloc(sizeof(RowNorm) * (size_t)(K + 1));
     for (int i = 0; i <= Ks; ++i) {
         Ct[i] = row_log_normaliser(target, dtype,
                                    (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride,
@@ -388,8 +404,8 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     for (int i = 0; i < Ks; ++i) {
         int64_t toff = (int64_t)s * t_batch_stride + (int64_t)i * t_row_stride;
         int64_t doff = (int64_t)s * d_batch_stride + (int64_t)i * d_row_stride;
-        double lp = logit_at(target, dtype, toff + x[i]) / T - Ct[i];
-        double lq = logit_at(draft, dtype, doff + x[i]) / Tq - Cd[i];
+        double lp = log_prob(logit_at(target, dtype, toff + x[i]), Ct[i], T);
+        double lq = log_prob(logit_at(draft, dtype, doff + x[i]), Cd[i], Tq);
         double p = exp(lp), q = exp(lq);
         double r;
         if (lp == -INFINITY) {
@@ -423,7 +439,10 @@ static void sample_sequence(const void *target, const void *draft, int dtype,
     int64_t toff = (int64_t)s * t_batch_stride + (int64_t)draw_row * t_row_stride;
     int64_t doff = (int64_t)s * d_batch_stride + (int64_t)(n < Ks ? n : 0) * d_row_stride;
     int residual = n < Ks;
-    double Cdn = residual ? Cd[n] : 0.0;
+    RowNorm Cdn = {0.0, 0.0};
+    if (residual) {
+        Cdn = Cd[n];
+    }
     double R = 0.0;
     for (int v = 0; v < V; ++v) {
         R += draw_weight(target, draft, dtype, toff, doff, v, T, Ct[draw_row], Cdn, residual);
@@ -584,8 +603,8 @@ int oracle_draw_cdf(const void *target, const void *draft, int dtype,
         return 1;
     }
     int64_t toff = (int64_t)s * t_batch_stride + (int64_t)slot * t_row_stride;
-    double Ct = row_log_normaliser(target, dtype, toff, V, T);
-    double Cd = 0.0;
+    RowNorm Ct = row_log_normaliser(target, dtype, toff, V, T);
+    RowNorm Cd = {0.0, 0.0};
     int64_t doff = 0;
     if (residual) {
         if (slot >= K) {
@@ -606,5 +625,6 @@ int oracle_draw_cdf(const void *target, const void *draft, int dtype,
  * independent library routine. */
 double oracle_row_log_normaliser(const void *base, int dtype, int V, double T)
 {
-    return row_log_normaliser(base, dtype, 0, V, T);
+    RowNorm n = row_log_normaliser(base, dtype, 0, V, T);
+    return n.M / T + n.L;
 }

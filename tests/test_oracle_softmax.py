@@ -90,3 +90,25 @@ def test_draw_cdf_rejects_bad_arguments(orc):
         orc.draw_cdf(target, draft, 0.0, 0, 0, False)        # T must be > 0
     with pytest.raises(ValueError):
         orc.draw_cdf(target, draft, 1.0, 0, 2, True)         # no residual at the bonus slot
+
+
+@pytest.mark.parametrize("offset", [0.0, 3.0e5, 2.0e6])
+def test_tied_maxima_at_a_tiny_temperature(orc, offset):
+    """Closed form: a row whose two largest logits are equal and every other
+    entry sits at least 1 below them has, at T = 1e-6, p = 1/2 at each
+    maximum (the rest weigh exp(-1e6)), whatever common offset the row
+    carries.  z / T reaches 2e12 at the largest offset, so a log-sum-exp
+    taken on z / T before the maximum is subtracted loses about 1e-4 here."""
+    V, T = 4099, 1.0e-6
+    rng = np.random.default_rng(17)
+    row = (offset + rng.uniform(-8.0, -1.0, V)).astype(np.float32)
+    top = np.float32(offset + 0.75)
+    row[[1000, 2048]] = top
+    target = np.stack([row, row]).reshape(1, 2, V)               # rows p_1 and the bonus row
+    draft = row.reshape(1, 1, V).copy()
+    for x in (1000, 2048):
+        res = orc.sample_accept(target, draft, np.array([[x]], np.int32), T, np.array([7], np.uint64))
+        assert res["p_draft"][0, 0] == pytest.approx(0.5, rel=1e-12)
+        assert res["q_draft"][0, 0] == pytest.approx(0.5, rel=1e-12)
+        assert res["n_accepted"][0] == 1                         # p(x) = q(x): always accepted
+    assert orc.row_log_normaliser(row, T) == pytest.approx(float(top) / T + np.log(2.0), rel=1e-15)
